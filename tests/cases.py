@@ -1,0 +1,88 @@
+"""Test cases: seeded inputs from the generator module, with the routing-score
+gap enforced by the oracle (a test-side step: the generator itself holds no
+routing arithmetic).  The k-th vs (k+1)-th selection score of every token, and
+for grouped routing the topk_group-th vs next group score, differ by at least
+MIN_GAP, so fp32 and fp64 routing cannot disagree.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from sparse_moe_transformer_sigmoid_amd import inputs as gen
+
+MIN_GAP = 1e-3
+
+
+def route_kwargs(wl: gen.Workload) -> dict:
+    return dict(num_experts_per_tok=wl.num_experts_per_tok, n_group=wl.n_group,
+                topk_group=wl.topk_group, norm_topk_prob=wl.norm_topk_prob,
+                routed_scaling_factor=wl.routed_scaling_factor)
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def bad_rows(wl, x64, router64, bias64):
+    r = oracle.route(x64, router64, bias64, **route_kwargs(wl))
+    gap = oracle.selection_gap(r, wl.num_experts_per_tok)
+    ggap = oracle.group_gap(r, wl.n_group, wl.topk_group)
+    return np.nonzero((gap < MIN_GAP) | (ggap < MIN_GAP))[0]
+
+
+def enforce_gap(wl: gen.Workload, x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor,
+                max_passes: int = 40) -> torch.Tensor:
+    """Redraw token rows of x (CPU tensor) until every token's gap >= MIN_GAP."""
+    x = x.clone()
+    r64, b64 = to64(router_w), to64(bias)
+    rows = np.arange(x.shape[0])
+    for attempt in range(max_passes):
+        bad = rows[bad_rows(wl, to64(x[rows]), r64, b64)]
+        if len(bad) == 0:
+            return x
+        x[bad] = gen.gen_x_rows(wl, bad, attempt)
+        rows = bad
+    raise RuntimeError(f"gap enforcement did not converge for {wl.name}")
+
+
+def make_case(wl: gen.Workload, device="cpu", num_tokens=None, gap=True) -> dict:
+    """Inputs of `wl` on `device`; x gap-enforced on the CPU first."""
+    x = gen.gen_x(wl, num_tokens)
+    rw, b = gen.gen_router(wl), gen.gen_bias(wl)
+    if gap and x.shape[0] > 0:
+        x = enforce_gap(wl, x, rw, b)
+    d = {"x": x.to(device), "router_w": rw.to(device), "router_bias": b.to(device)}
+    d.update(gen.gen_expert_weights(wl, device))
+    return d
+
+
+def expert_fn(wl: gen.Workload, case: dict):
+    """Oracle callback: routed expert e's fp64 (gate, up, down), one at a time."""
+    fp8 = wl.weight_dtype == gen.FP8
+
+    def mat(name, e):
+        w = case["w_" + name][e]
+        if fp8:
+            return oracle.dequant_weight(w.cpu().numpy(), case["s_" + name][e].cpu().numpy())
+        return to64(w)
+
+    return lambda e: (mat("gate", e), mat("up", e), mat("down", e))
+
+
+def shared_weights(wl: gen.Workload, case: dict):
+    if wl.n_shared_experts == 0:
+        return None
+    if wl.weight_dtype == gen.FP8:
+        return tuple(oracle.dequant_weight(case["sh_" + n].cpu().numpy(), case["sh_s_" + n].cpu().numpy())
+                     for n in ("gate", "up", "down"))
+    return tuple(to64(case["sh_" + n]) for n in ("gate", "up", "down"))
+
+
+def oracle_forward(wl: gen.Workload, case: dict, tokens=None):
+    """fp64 oracle output (and Route) of `case`, optionally for a token subset."""
+    return oracle.layer_forward(
+        to64(case["x"]), to64(case["router_w"]), to64(case["router_bias"]),
+        expert_fn(wl, case), shared_weights(wl, case), fp8_act=(wl.weight_dtype == gen.FP8),
+        tokens=tokens, **route_kwargs(wl))

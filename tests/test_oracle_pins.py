@@ -1,0 +1,484 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+Each test names the passage (page title + table/section) or the closed form it
+checks.  No expected value here comes from the HIP path or from the oracle
+itself: they are page-printed numbers, hand-derived closed forms, brute force
+over all subsets, or independent library routines (torch fp64, torch's e4m3
+cast).  test_planted_mistakes_are_caught plants plausible bugs in the oracle
+and checks that some pin fails for each.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import moe_oracle as om
+from sparse_moe_transformer_sigmoid_amd import inputs as gen
+import cases
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- P1 / P2 --
+def check_param_counts():
+    g = gold("down_proj_params.json")
+    assert om.linear_params(g["out_features"], g["in_features"]) == g["per_instance"]
+    assert om.linear_params(g["out_features"], g["in_features"]) * g["n_experts"] == g["per_layer_384_experts"]
+    assert (om.linear_params(g["out_features"], g["in_features"]) * g["n_experts"] * g["moe_blocks"]
+            == g["all_60_moe_blocks"])
+    c = gold("k2_config_fields.json")
+    # gate/up are [F, H], down is [H, F]: three equal-size linears per expert
+    assert om.expert_params(c["hidden_size"], c["moe_intermediate_size"]) == 3 * g["per_instance"]
+
+
+def test_p1_param_counts_match_down_projection_page():
+    check_param_counts()
+
+
+def test_p1_k2_workload_fields_match_config_table():
+    c = gold("k2_config_fields.json")
+    for name in ("k2_decode_bf16", "k2_prefill_bf16_zipf", "k2_fp8"):
+        f = gen.WORKLOADS[name].fields()
+        for key in ("hidden_size", "moe_intermediate_size", "n_routed_experts", "num_experts_per_tok",
+                    "n_shared_experts", "n_group", "topk_group", "norm_topk_prob", "routed_scaling_factor"):
+            assert f[key] == c[key], (name, key)
+        assert gen.WORKLOADS[name].weight_std == c["initializer_range"]
+
+
+def check_ep128_footprint():
+    g = gold("ep128_footprint.json")
+    c = gold("k2_config_fields.json")
+    wbytes, sbytes = om.fp8_expert_bytes(c["hidden_size"], c["moe_intermediate_size"])
+    assert wbytes == 44_040_192 and sbytes == 10_752
+    dsv3 = g["dsv3_experts_per_rank"] * (g["num_hidden_layers"] - g["dsv3_dense_layers"]) * wbytes / 1e9
+    k2 = g["k2_experts_per_rank"] * (g["num_hidden_layers"] - g["k2_dense_layers"]) * wbytes / 1e9
+    # the page's figures are rounded ("about"); 1 B/param fp8 and a shared
+    # expert as large as a routed one land within 10 % of both
+    assert abs(dsv3 - g["dsv3_gb_approx"]) / g["dsv3_gb_approx"] < 0.10
+    assert abs(k2 - g["k2_gb_approx"]) / g["k2_gb_approx"] < 0.10
+    assert abs((k2 - dsv3) - g["extra_gb_approx"]) / g["extra_gb_approx"] < 0.25
+
+
+def test_p2_ep128_footprints_match_section_2_1():
+    check_ep128_footprint()
+
+
+def test_p12_prefill_flop_ratio_closed_form():
+    # activated flops per token barely change between 256 and 384 experts
+    # ("Behind Kimi-K2's Config", section 2.1, Prefill bullet)
+    k2 = om.layer_flops(1, 7168, 2048, 384, 8, 1)
+    ds = om.layer_flops(1, 7168, 2048, 256, 8, 1)
+    assert k2 == 9 * 2 * 3 * 7168 * 2048 + 2 * 7168 * 384
+    assert abs(k2 / ds - 1.0023) < 1e-4
+
+
+# --------------------------------------------------------- worked examples --
+def check_routing_worked_example():
+    """Hand-derived: sigmoid(ln a) = a / (1 + a).
+
+    logits = [0, ln 3, -ln 3, ln 9] -> scores [1/2, 3/4, 1/4, 9/10].
+    bias   = [0.5, 0, 0.3, -0.5]    -> sel    [1.0, 0.75, 0.55, 0.4].
+    top-2 by sel = {0, 1} (without the bias it would be {1, 3}); weights use
+    the unbiased scores: [0.5, 0.75] / 1.25 * 2.827 = [1.1308, 1.6962].
+    """
+    x = np.array([[1.0]])
+    w = np.array([[0.0], [math.log(3)], [-math.log(3)], [math.log(9)]])
+    b = np.array([0.5, 0.0, 0.3, -0.5])
+    r = oracle.route(x, w, b, num_experts_per_tok=2, routed_scaling_factor=2.827)
+    assert r.ids.tolist() == [[0, 1]]
+    np.testing.assert_allclose(r.weights, [[0.4 * 2.827, 0.6 * 2.827]], rtol=1e-14)
+    r0 = oracle.route(x, w, np.zeros(4), num_experts_per_tok=2, routed_scaling_factor=2.827)
+    assert r0.ids.tolist() == [[1, 3]]
+    np.testing.assert_allclose(r0.weights, [[0.75 / 1.65 * 2.827, 0.9 / 1.65 * 2.827]], rtol=1e-14)
+    # norm_topk_prob false: the scaled raw scores
+    r1 = oracle.route(x, w, b, num_experts_per_tok=2, norm_topk_prob=False, routed_scaling_factor=2.0)
+    np.testing.assert_allclose(r1.weights, [[1.0, 1.5]], rtol=1e-14)
+
+
+def test_routing_worked_example():
+    check_routing_worked_example()
+
+
+def check_swiglu_worked_example():
+    """Hand-derived: x = [2, 0]; W_gate = [[ln3 / 2, 5]] -> g = ln 3;
+    W_up = [[1, 7]] -> u = 2; silu(ln 3) = ln 3 * 3/4; h = 1.5 ln 3;
+    W_down = [[1], [-2]] -> y = [1.5 ln 3, -3 ln 3]."""
+    x = np.array([[2.0, 0.0]])
+    y = om.swiglu_expert(x, np.array([[math.log(3) / 2, 5.0]]), np.array([[1.0, 7.0]]),
+                         np.array([[1.0], [-2.0]]))
+    np.testing.assert_allclose(y, [[1.5 * math.log(3), -3 * math.log(3)]], rtol=1e-14)
+
+
+def test_swiglu_worked_example():
+    check_swiglu_worked_example()
+
+
+# ---------------------------------------------------------------- P3 / P4 --
+def tiny_router(seed=0, T=64, E=16, H=32, bias_std=0.01):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((T, H)), rng.standard_normal((E, H)) * 0.3, rng.standard_normal(E) * bias_std
+
+
+def check_routing_invariants(x, w, b, k, **kw):
+    r = oracle.route(x, w, b, num_experts_per_tok=k, **kw)
+    T, E = r.scores.shape
+    assert r.ids.shape == (T, k)
+    for t in range(T):
+        assert len(set(r.ids[t].tolist())) == k
+        assert np.all(np.diff(r.ids[t]) > 0)
+    np.testing.assert_allclose(r.weights.sum(1), kw.get("routed_scaling_factor", 2.827), rtol=1e-12)
+    assert np.all(r.weights > 0)
+    offsets, sorted_ids, inv = oracle.permute(r.ids, E)
+    assert offsets[-1] == k * T and np.bincount(r.ids.ravel(), minlength=E).sum() == k * T
+    # chosen experts' sel dominate the unchosen eligible ones
+    for t in range(T):
+        chosen = np.zeros(E, bool)
+        chosen[r.ids[t]] = True
+        others = r.sel[t][~chosen & r.eligible[t]]
+        if len(others):
+            assert r.sel[t][chosen].min() >= others.max()
+    return r
+
+
+def test_p3_routing_invariants_tiny_and_k2_router():
+    x, w, b = tiny_router()
+    check_routing_invariants(x, w, b, 4)
+    wl = gen.WORKLOADS["k2_decode_bf16"]
+    xr = cases.to64(gen.gen_x(wl, 64))
+    check_routing_invariants(xr, cases.to64(gen.gen_router(wl)), cases.to64(gen.gen_bias(wl)), 8)
+
+
+def check_bruteforce_topk(seed=1, k=4):
+    x, w, b = tiny_router(seed, T=24)
+    r = oracle.route(x, w, b, num_experts_per_tok=k)
+    E = w.shape[0]
+    for t in range(x.shape[0]):
+        best = max(itertools.combinations(range(E), k), key=lambda s: r.sel[t, list(s)].sum())
+        assert list(best) == r.ids[t].tolist()
+        # weights: unbiased scores of the chosen set, renormalised, scaled
+        s = 1.0 / (1.0 + np.exp(-(w[list(best)] @ x[t])))
+        np.testing.assert_allclose(r.weights[t], s / s.sum() * 2.827, rtol=1e-12)
+
+
+def test_p4_bruteforce_topk_all_subsets():
+    check_bruteforce_topk()
+
+
+def check_bruteforce_grouped(seed=2, E=16, n_group=4, topk_group=2, k=4):
+    x, w, b = tiny_router(seed, T=24, E=E, bias_std=0.3)
+    r = oracle.route(x, w, b, num_experts_per_tok=k, n_group=n_group, topk_group=topk_group)
+    gsz = E // n_group
+    for t in range(x.shape[0]):
+        sel = r.sel[t]
+        # a group's score: the best pair of sel values inside it
+        gscore = [max(sel[g * gsz + i] + sel[g * gsz + j] for i in range(gsz) for j in range(i + 1, gsz))
+                  for g in range(n_group)]
+        gbest = max(itertools.combinations(range(n_group), topk_group), key=lambda s: sum(gscore[i] for i in s))
+        allowed = [e for g in gbest for e in range(g * gsz, (g + 1) * gsz)]
+        best = max(itertools.combinations(allowed, k), key=lambda s: sel[list(s)].sum())
+        assert sorted(best) == r.ids[t].tolist()
+
+
+def test_p4_bruteforce_grouped_topk():
+    check_bruteforce_grouped()
+
+
+# --------------------------------------------------------------------- P5 --
+def test_p5_grouping_that_keeps_every_group_is_ungrouped():
+    x, w, b = tiny_router(3)
+    r0 = oracle.route(x, w, b, num_experts_per_tok=4)
+    for ng in (2, 4, 16):
+        r = oracle.route(x, w, b, num_experts_per_tok=4, n_group=ng, topk_group=ng)
+        assert np.array_equal(r.ids, r0.ids)
+        np.testing.assert_array_equal(r.weights, r0.weights)
+
+
+def test_p5_zero_bias_selects_topk_logits():
+    x, w, _ = tiny_router(4)
+    r = oracle.route(x, w, np.zeros(w.shape[0]), num_experts_per_tok=4)
+    logits = x @ w.T
+    expect = np.sort(np.argsort(logits, axis=1)[:, -4:], axis=1)
+    assert np.array_equal(r.ids, expect)
+
+
+# ------------------------------------------------------------- P6 / P7 / P8 --
+def torch_swiglu(x, wg, wu, wd):
+    """Independent fp64 SwiGLU via torch library routines."""
+    X = torch.from_numpy(np.asarray(x, np.float64))
+    g = torch.matmul(X, torch.from_numpy(wg).T)
+    u = torch.matmul(X, torch.from_numpy(wu).T)
+    return torch.matmul(torch.nn.functional.silu(g) * u, torch.from_numpy(wd).T).numpy()
+
+
+def small_weights(seed, E, H=24, F=16, Fs=16):
+    rng = np.random.default_rng(seed)
+    ex = [tuple(rng.standard_normal(s) * 0.2 for s in ((F, H), (F, H), (H, F))) for _ in range(E)]
+    sh = tuple(rng.standard_normal(s) * 0.2 for s in ((Fs, H), (Fs, H), (H, Fs)))
+    return ex, sh
+
+
+def check_identical_experts(seed=5):
+    rng = np.random.default_rng(seed)
+    T, H, E, k = 20, 24, 8, 3
+    x = rng.standard_normal((T, H))
+    rw, b = rng.standard_normal((E, H)) * 0.3, rng.standard_normal(E) * 0.1
+    ex, sh = small_weights(seed, 1, H)
+    out, _ = oracle.layer_forward(x, rw, b, lambda e: ex[0], sh, num_experts_per_tok=k)
+    expect = torch_swiglu(x, *sh) + 2.827 * torch_swiglu(x, *ex[0])
+    np.testing.assert_allclose(out, expect, rtol=1e-12, atol=1e-12)
+
+
+def test_p6_identical_experts_closed_form():
+    check_identical_experts()
+
+
+def check_single_expert(seed=6):
+    rng = np.random.default_rng(seed)
+    T, H = 9, 24
+    x = rng.standard_normal((T, H))
+    ex, sh = small_weights(seed, 1, H, F=16, Fs=32)
+    out, r = oracle.layer_forward(x, rng.standard_normal((1, H)), np.zeros(1), lambda e: ex[0], sh,
+                                  num_experts_per_tok=1)
+    assert np.all(r.ids == 0) and np.allclose(r.weights, 2.827)
+    np.testing.assert_allclose(out, torch_swiglu(x, *sh) + 2.827 * torch_swiglu(x, *ex[0]),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_p7_single_expert_is_textbook_swiglu():
+    check_single_expert()
+
+
+def test_p8_zero_input_and_invariances():
+    rng = np.random.default_rng(7)
+    T, H, E, k = 12, 24, 8, 3
+    rw, b = rng.standard_normal((E, H)) * 0.3, rng.standard_normal(E) * 0.1
+    ex, sh = small_weights(7, E, H)
+    fwd = lambda xx: oracle.layer_forward(xx, rw, b, lambda e: ex[e], sh, num_experts_per_tok=k)[0]
+    assert np.all(fwd(np.zeros((3, H))) == 0.0)
+    x = rng.standard_normal((T, H))
+    full = fwd(x)
+    perm = rng.permutation(T)
+    np.testing.assert_allclose(fwd(x[perm]), full[perm], rtol=1e-12, atol=1e-13)
+    for t in range(T):
+        np.testing.assert_allclose(fwd(x[t:t + 1])[0], full[t], rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------- P9 --
+def all_e4m3_values():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return codes, vals
+
+
+def check_e4m3():
+    codes, tv = all_e4m3_values()
+    ov = om.e4m3_decode(codes)
+    finite = ~np.isnan(tv)
+    assert np.array_equal(np.isnan(ov), ~finite)
+    np.testing.assert_array_equal(ov[finite], tv[finite])
+    assert np.nanmax(tv) == 448.0
+    # every representable value round-trips exactly
+    np.testing.assert_array_equal(om.e4m3_round(tv[finite]), tv[finite])
+    # midpoints (ties) and random values vs torch's RNE cast after clamping
+    pos = np.unique(np.abs(tv[finite]))
+    mids = (pos[1:] + pos[:-1]) / 2
+    rng = np.random.default_rng(0)
+    rnd = np.concatenate([rng.uniform(-500, 500, 20000), rng.standard_normal(20000) * 0.01,
+                          rng.standard_normal(2000) * 1e-3, mids, -mids, [0.0, 447.9, 448.0, 460.0, 470.0, 1e6]])
+    rnd = rnd.astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(np.clip(rnd, -448, 448)).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(om.e4m3_round(rnd), ref)
+
+
+def test_p9_e4m3_matches_torch_cast():
+    check_e4m3()
+
+
+def test_p9_activation_quant_properties():
+    rng = np.random.default_rng(8)
+    v = (rng.standard_normal((5, 256)) * np.array([1.0, 1e-3, 10.0, 0.0, 1.0])[:, None]).astype(np.float32)
+    deq, q, s = om.act_quant(v)
+    assert s.dtype == np.float32 and s.shape == (5, 2)
+    assert np.all(s[3] == 1.0) and np.all(deq[3] == 0.0)
+    # each group's largest magnitude maps to +-448 and nothing exceeds it
+    g = np.abs(q.reshape(5, 2, 128))
+    assert np.all(g.max(axis=2)[[0, 1, 2, 4]] == 448.0) and g.max() <= 448.0
+    # reconstruction error <= half an e4m3 step (relative 2^-4) plus subnormal floor
+    err = np.abs(deq - v.astype(np.float64))
+    bound = np.abs(v) * 2.0 ** -4 + np.repeat(s.astype(np.float64), 128, axis=1) * 2.0 ** -10
+    assert np.all(err <= bound * (1 + 1e-6))
+
+
+def test_p9_block_dequant_matches_decode_times_scale():
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 256, (256, 384)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    scales = rng.uniform(0.5, 2, (2, 3)).astype(np.float32)
+    w = om.dequant_weight(codes, scales)
+    tv = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for i in range(2):
+        for j in range(3):
+            np.testing.assert_array_equal(w[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128],
+                                          tv[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128] * float(scales[i, j]))
+
+
+# -------------------------------------------------------------------- P10 --
+def check_permutation(seed=10):
+    x, w, b = tiny_router(seed, T=40)
+    r = oracle.route(x, w, b, num_experts_per_tok=4)
+    E, (T, k) = w.shape[0], r.ids.shape
+    offsets, sorted_ids, inv = oracle.permute(r.ids, E)
+    # brute force: walk experts in order, tokens in order
+    pos, want_sorted, want_inv = 0, [], np.zeros(T * k, int)
+    for e in range(E):
+        assert offsets[e] == pos
+        for t in range(T):
+            for j in range(k):
+                if r.ids[t, j] == e:
+                    want_sorted.append(t)
+                    want_inv[t * k + j] = pos
+                    pos += 1
+    assert offsets[E] == pos == T * k
+    assert sorted_ids.tolist() == want_sorted
+    assert inv.tolist() == want_inv.tolist()
+
+
+def test_p10_stable_permutation_bruteforce():
+    check_permutation()
+
+
+# -------------------------------------------------------------------- P11 --
+def test_p11_active_expert_count_matches_expectation():
+    # decode bytes scale with the number of distinct experts touched,
+    # E (1 - (1 - k/E)^T) for independent uniform picks ("Behind Kimi-K2's
+    # Config", section 2.1, Decode bullet: time follows parameters read).
+    # With a zero correction bias the random router is close to uniform; the
+    # N(0, 0.01) bias of the workloads skews it (fewer experts touched), which
+    # is why measured bytes use the realised count.
+    wl = gen.WORKLOADS["k2_decode_bf16"].replace(bias="zero")
+    rw, b = cases.to64(gen.gen_router(wl)), cases.to64(gen.gen_bias(wl))
+    for T in (32, 128):
+        x = cases.to64(gen.gen_x(wl, T))
+        r = oracle.route(x, rw, b, num_experts_per_tok=8)
+        active = len(np.unique(r.ids))
+        expect = 384 * (1 - (1 - 8 / 384) ** T)
+        assert abs(active - expect) < 0.04 * expect, (T, active, expect)
+
+
+# ------------------------------------------------------------ fp8 layer ----
+def test_fp8_layer_matches_dequantised_reference():
+    """fp8 mode = the same layer on q*s weights and q*s activations: with
+    activation quantisation switched on, every expert sees act_quant(x) and
+    act_quant(h).  Checked against torch fp64 on those dequantised inputs."""
+    wl = gen.WORKLOADS["small_fp8"].replace(num_tokens=6)
+    case = cases.make_case(wl)
+    out, r = cases.oracle_forward(wl, case)
+    ex, sh = cases.expert_fn(wl, case), cases.shared_weights(wl, case)
+    xq = om.act_quant(cases.to64(case["x"]))[0]
+
+    def f(xx, wg, wu, wd):
+        X = torch.from_numpy(xx)
+        h = torch.nn.functional.silu(X @ torch.from_numpy(wg).T) * (X @ torch.from_numpy(wu).T)
+        h = torch.from_numpy(om.act_quant(h.numpy())[0])
+        return (h @ torch.from_numpy(wd).T).numpy()
+
+    expect = f(xq, *sh)
+    for t in range(6):
+        for j, e in enumerate(r.ids[t]):
+            expect[t] += r.weights[t, j] * f(xq[t:t + 1], *ex(int(e)))[0]
+    np.testing.assert_allclose(out, expect, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------ planted mistakes ---
+PINS = [check_param_counts, check_routing_worked_example, check_swiglu_worked_example,
+        check_bruteforce_topk, check_bruteforce_grouped, check_identical_experts,
+        check_single_expert, check_e4m3, check_permutation]
+
+
+def _any_pin_fails():
+    for p in PINS:
+        try:
+            p()
+        except AssertionError:
+            return True
+    return False
+
+
+MUTANTS = {
+    "weights_from_biased_scores": ("route", lambda orig: (
+        lambda x, w, b, **kw: _weights_from(orig(x, w, b, **kw), "sel", kw))),
+    "no_renormalisation": ("route", lambda orig: (
+        lambda x, w, b, **kw: orig(x, w, b, **{**kw, "norm_topk_prob": False}))),
+    "bottom_k": ("_top_indices", lambda orig: (lambda v, n: orig(-v, n))),
+    "silu_sign": ("silu", lambda orig: (lambda z: z / (1.0 + np.exp(z)))),
+    "drop_shared": ("swiglu_expert", None),
+    "gate_up_swapped": ("swiglu_expert", lambda orig: (
+        lambda x, wg, wu, wd, fp8_act=False: orig(x, wu, wg, wd, fp8_act))),
+    "group_max_not_top2": ("group_scores", lambda orig: (
+        lambda sel, ng: np.sort(sel.reshape(sel.shape[0], ng, -1), axis=2)[:, :, -1])),
+    "e4m3_truncate": ("e4m3_round", lambda orig: (lambda v: _trunc_e4m3(v))),
+    "permute_unstable": ("permute", lambda orig: (lambda ids, E: _unstable_permute(orig, ids, E))),
+    "expert_params_two_linears": ("expert_params", lambda orig: (lambda h, f: 2 * h * f)),
+}
+
+
+def _weights_from(r, field, kw):
+    w = np.take_along_axis(getattr(r, field), r.ids, axis=1)
+    r.weights = w / w.sum(1, keepdims=True) * kw.get("routed_scaling_factor", 2.827)
+    return r
+
+
+def _trunc_e4m3(v):
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    q = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)
+    return np.copysign(np.minimum(np.floor(a / q) * q, 448.0), v)
+
+
+def _unstable_permute(orig, ids, E):
+    offsets, s, inv = orig(ids, E)
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        s[a:b] = s[a:b][::-1]
+    return offsets, s, inv
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistakes_are_caught(mutant, monkeypatch):
+    assert not _any_pin_fails()
+    fname, make = MUTANTS[mutant]
+    orig = getattr(om, fname)
+    if mutant == "drop_shared":
+        calls = {"n": 0}
+
+        def patched(x, wg, wu, wd, fp8_act=False):
+            calls["n"] += 1
+            y = orig(x, wg, wu, wd, fp8_act)
+            return 0 * y if calls["n"] == 1 else y
+        # the first expert evaluated in layer_forward is the shared one
+        monkeypatch.setattr(om, "layer_forward", _fresh_counter(om.layer_forward, calls))
+        monkeypatch.setattr(om, fname, patched)
+    else:
+        monkeypatch.setattr(om, fname, make(orig))
+    monkeypatch.setattr(oracle, fname, getattr(om, fname), raising=False)
+    if hasattr(oracle, "layer_forward"):
+        monkeypatch.setattr(oracle, "layer_forward", om.layer_forward)
+    assert _any_pin_fails(), f"planted mistake {mutant} went unnoticed"
+
+
+def _fresh_counter(fn, calls):
+    def wrapped(*a, **kw):
+        calls["n"] = 0
+        return fn(*a, **kw)
+    return wrapped
