@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the Kimi-K2 routed MoE FFN layer on one MI355X.
+
+One step = one moe_layer_forward (router, grouping, expert FFNs, combine) over
+one batch of synthetic tokens whose inputs are already resident in HBM.
+Default workload: Kimi-K2 decode, T = 128 tokens, bf16, all 384 experts + 1
+shared resident.  Prints ONE JSON line (value = tokens/s) with:
+  roofline      -- the dominant kernel (grouped gate_up GEMM): algorithmic
+                   bytes or flops per launch / its mean duration, timed with
+                   HIP events the library records around that launch;
+  cpu_baseline  -- the fp64 oracle timed on a bounded sample of the same
+                   workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_moe_transformer_sigmoid_amd import binding as B  # noqa: E402
+from sparse_moe_transformer_sigmoid_amd import inputs as gen  # noqa: E402
+
+METRIC = "MoE-layer tokens/s; % HBM peak (decode T=128), % MFMA peak (prefill T=8192)"
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {gen.BF16: 2500.0, gen.FP8: 5000.0, gen.F32: 157.3}
+KERNEL_SOURCES = ["ffn_stream.hip", "ffn_tile.hip", "ffn_fp8.hip", "common.h"]
+
+
+class Hip:
+    """Raw hipEvent handles (the library records them on its own stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+
+    def event(self) -> int:
+        ev = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def setup(wl: gen.Workload, T: int):
+    x = gen.gen_x(wl, T).cuda()
+    d = {"x": x, "router_w": gen.gen_router(wl).cuda(), "router_bias": gen.gen_bias(wl).cuda()}
+    d.update(gen.gen_expert_weights(wl, device="cuda"))
+    torch.cuda.synchronize()
+    return d
+
+
+def weight_bytes_per_expert_gate_up(wl: gen.Workload, F: int) -> int:
+    H = wl.hidden_size
+    if wl.weight_dtype == gen.FP8:
+        return 2 * F * H + 2 * (F // 128) * (H // 128) * 4
+    return 2 * F * H * (4 if wl.weight_dtype == gen.F32 else 2)
+
+
+def roofline(wl: gen.Workload, T: int, n_active: int, gate_up_ms: float, traffic):
+    """Algorithmic work of one gate_up launch against the bound it sits on."""
+    F, Fs, H, k = wl.moe_intermediate_size, wl.shared_intermediate_size, wl.hidden_size, wl.num_experts_per_tok
+    bytes_ = n_active * weight_bytes_per_expert_gate_up(wl, F)
+    if Fs:
+        bytes_ += weight_bytes_per_expert_gate_up(wl, Fs)
+    flops = 4.0 * (T * k * F + T * Fs) * H
+    peak_tf = PEAK_TFLOPS[wl.weight_dtype]
+    ridge = peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
+    sec = gate_up_ms * 1e-3
+    if flops / bytes_ > ridge:
+        ach = flops / sec / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(ach / peak_tf, 4), "traffic": traffic,
+                "kernel": "gate_up", "kernel_ms": round(gate_up_ms, 4), "algorithmic_flops": flops}
+    ach = bytes_ / sec / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "kernel": "gate_up", "kernel_ms": round(gate_up_ms, 4), "algorithmic_bytes": bytes_}
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per gate_up launch measured by rocprofv3 counters, if they were
+    taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    return d.get("traffic_bytes") if d.get("kernel_hash") == kernel_hash() else None
+
+
+def cpu_baseline(wl, case, T, budget_s):
+    """The fp64 oracle (as it stands) on a bounded sample of the same tokens."""
+    import threadpoolctl
+    import oracle
+    x64 = case["x"].double().cpu().numpy()
+    rw = case["router_w"].double().cpu().numpy()
+    b = case["router_bias"].double().cpu().numpy()
+    kw = dict(num_experts_per_tok=wl.num_experts_per_tok, n_group=wl.n_group, topk_group=wl.topk_group,
+              norm_topk_prob=wl.norm_topk_prob, routed_scaling_factor=wl.routed_scaling_factor)
+    fp8 = wl.weight_dtype == gen.FP8
+    # one token first to size the sample to the time budget
+    n = 1
+    while True:
+        toks = np.linspace(0, T - 1, n).astype(np.int64) if n > 1 else np.array([0])
+        need = np.unique(oracle.route(x64[toks], rw, b, **kw).ids)
+        host = {}
+        for e in need:  # host copies of the stored weights (outside the timed region)
+            host[int(e)] = {m: case["w_" + m][e].cpu() for m in ("gate", "up", "down")}
+            if fp8:
+                host[int(e)].update({"s_" + m: case["s_" + m][e].cpu() for m in ("gate", "up", "down")})
+        sh = {m: case["sh_" + m].cpu() for m in ("gate", "up", "down")}
+        if fp8:
+            sh.update({"s_" + m: case["sh_s_" + m].cpu() for m in ("gate", "up", "down")})
+
+        def mat(d, m):
+            if fp8:
+                return oracle.dequant_weight(d[m].numpy(), d["s_" + m].numpy())
+            return d[m].to(torch.float64).numpy()
+
+        t0 = time.perf_counter()
+        oracle.layer_forward(x64, rw, b, lambda e: tuple(mat(host[e], m) for m in ("gate", "up", "down")),
+                             tuple(mat(sh, m) for m in ("gate", "up", "down")) if wl.n_shared_experts else None,
+                             fp8_act=fp8, tokens=toks, **kw)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 3 or n >= T or n >= 64:
+            break
+        n = min(T, max(n + 1, int(n * budget_s / max(dt, 1e-3) * 0.5)), 64)
+    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
+        if threadpoolctl.threadpool_info() else 1
+    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of the {T} tokens (evenly spaced), {len(need)} routed experts + shared, "
+                      f"fp64 numpy, {dt:.1f} s", "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="k2_decode_bf16", choices=sorted(gen.WORKLOADS))
+    ap.add_argument("--tokens", type=int, default=None, help="override the workload's token count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--breakdown", action="store_true", help="per-kernel times to stderr")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--extra-out", default=None, help="append a detail JSON line to this file")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+              "(the layer runs unsharded on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    wl = gen.WORKLOADS[args.workload]
+    T = args.tokens or wl.num_tokens
+    hip = Hip()
+    B.load()
+    case = setup(wl, T)
+    cfg = B.MoeConfig.from_fields(wl.fields())
+    weights = B.MoeWeights.from_tensors(case)
+    out = torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda")
+    ids = torch.empty((T, wl.num_experts_per_tok), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, wl.num_experts_per_tok), dtype=torch.float32, device="cuda")
+    ws = B.alloc_workspace(cfg, T)
+
+    def step():
+        B.moe_layer_forward(cfg, weights, case["x"], case["router_w"], case["router_bias"], out, ws, ids, wts)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_active = int(torch.unique(ids).numel())
+
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        B.moe_profile_arm(B.MOE_KID_GATE_UP, *evs[i])
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))
+    ms_per_step = wall * 1e3 / args.steps
+
+    detail = {}
+    if args.breakdown:
+        names = ["router_logits", "router_topk", "permute", "tiles", "gather", "act_quant", "gate_up", "down",
+                 "combine"]
+        per = {n: [] for n in names}
+        for _ in range(5):
+            pairs = [(hip.event(), hip.event()) for _ in names]
+            for kid, (a, b) in enumerate(pairs):
+                B.moe_profile_arm(kid, a, b)
+            step()
+            torch.cuda.synchronize()
+            for kid, (a, b) in enumerate(pairs):
+                try:
+                    per[names[kid]].append(hip.elapsed_ms(a, b))
+                except AssertionError:
+                    pass
+            for kid in range(len(names)):
+                B.moe_profile_arm(kid, None, None)
+        detail = {n: round(float(np.median(v)), 4) for n, v in per.items() if v}
+        print(f"[breakdown ms] {detail}", file=sys.stderr)
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    rl = roofline(wl, T, n_active, gate_up_ms, stored_traffic(args.workload))
+    res = {
+        "metric": METRIC, "value": round(T * args.steps / wall, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if wl.weight_dtype == gen.FP8 else wl.act_dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "num_tokens": T, "hidden_size": wl.hidden_size,
+                   "moe_intermediate_size": wl.moe_intermediate_size, "n_routed_experts": wl.n_routed_experts,
+                   "num_experts_per_tok": wl.num_experts_per_tok, "n_shared_experts": wl.n_shared_experts,
+                   "n_group": wl.n_group, "topk_group": wl.topk_group, "active_experts": n_active,
+                   "parallelism": "none (one GPU, all experts resident)"},
+        "roofline": rl,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, case, T, args.cpu_budget)
+    if args.extra_out:
+        with open(args.extra_out, "a") as f:
+            f.write(json.dumps({**res, "breakdown_ms": detail, "kernel_hash": kernel_hash()}) + "\n")
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

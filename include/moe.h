@@ -1,0 +1,177 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the Kimi-K2 routed mixture-of-experts FFN layer
+ * (sigmoid scoring, correction-bias top-k, renormalised and scaled weights,
+ * SwiGLU experts plus a shared expert) as hand-written HIP kernels for gfx950.
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller, row-major,
+ *    16-byte aligned.  The library never allocates, frees or synchronises;
+ *    every call only enqueues kernels on `stream` (a hipStream_t passed as
+ *    void*, NULL = the null stream) and returns.
+ *  - Scratch memory is a caller-owned device workspace of at least
+ *    moe_workspace_size(cfg, num_tokens) bytes (256-byte aligned).  Calls that
+ *    share a workspace must be ordered (same stream).  No entry point uses
+ *    hipMemset, so a caller may capture a whole call in a HIP graph.
+ *  - Arguments are validated on the host before anything is launched; a bad
+ *    argument returns an error code and launches nothing.  num_tokens == 0 is
+ *    a no-op that returns MOE_OK.  moe_last_error() gives a message for the
+ *    last failure on the calling thread.
+ *  - Launch failures (hipGetLastError after a launch) return MOE_ERR_HIP.
+ *  - num_tokens is at most 65536.
+ *
+ * Shapes: T = num_tokens, H = hidden_size, F = moe_intermediate_size,
+ * E = n_routed_experts, k = num_experts_per_tok, Fs = n_shared_experts * F.
+ * Field names follow the model config tables ("Kimi K2 Base" / "Kimi K2 0905"
+ * raw config fields).  Linear weights are [out][in] without bias ("Kimi K2 .
+ * Down projection": "[out, in]", no bias parameter).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but not implemented (dtype, scoring)    */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes < moe_workspace_size(cfg, T)        */
+  MOE_ERR_HIP = 4          /* a HIP launch failed                          */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+
+/* scoring_func / topk_method values (raw config fields: scoring_func sigmoid,
+ * topk_method noaux_tc are the only ones accepted). */
+enum { MOE_SCORING_SIGMOID = 0 };
+enum { MOE_TOPK_NOAUX_TC = 0 };
+
+typedef struct {
+  int32_t hidden_size;           /* H; multiple of 128                          */
+  int32_t moe_intermediate_size; /* F; multiple of 128                          */
+  int32_t n_routed_experts;      /* E; 1..1023                                  */
+  int32_t num_experts_per_tok;   /* k; 1..min(E, 32)                            */
+  int32_t n_shared_experts;      /* 0..8; shared width Fs = n_shared * F         */
+  int32_t n_group;               /* >= 1, divides E, <= 64                       */
+  int32_t topk_group;            /* 1..n_group; k <= topk_group * E / n_group    */
+  int32_t norm_topk_prob;        /* 1: renormalise the k weights to sum 1        */
+  float routed_scaling_factor;   /* 2.827 for K2                                 */
+  int32_t scoring_func;          /* MOE_SCORING_SIGMOID                          */
+  int32_t topk_method;           /* MOE_TOPK_NOAUX_TC                            */
+  int32_t act_dtype;             /* x, router weight, y, out: MOE_F32 / MOE_BF16 */
+  int32_t weight_dtype;          /* expert weights: MOE_F32 / MOE_BF16 / MOE_FP8_E4M3 */
+  int32_t weight_block_size[2];  /* {128,128} for MOE_FP8_E4M3, else {0,0}       */
+} moe_config_t;
+/* Accepted dtype pairs (act, weight): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3). */
+
+typedef struct {
+  /* routed experts, [E][F][H], [E][F][H], [E][H][F] of weight_dtype */
+  const void *w_gate, *w_up, *w_down;
+  /* FP8 only: fp32 block scales [E][F/128][H/128], same, [E][H/128][F/128] */
+  const float *s_gate, *s_up, *s_down;
+  /* shared expert: [Fs][H], [Fs][H], [H][Fs]; NULL when n_shared_experts == 0 */
+  const void *sh_gate, *sh_up, *sh_down;
+  /* FP8 only: [Fs/128][H/128], same, [H/128][Fs/128] */
+  const float *sh_s_gate, *sh_s_up, *sh_s_down;
+} moe_weights_t;
+
+/* Bytes of workspace every entry point below needs for T tokens (the maximum
+ * over the entry points, so one workspace serves all of them). */
+size_t moe_workspace_size(const moe_config_t* cfg, int64_t num_tokens);
+
+/* Router ("Kimi K2 Base"/"Kimi K2 0905" raw config fields: scoring_func
+ * sigmoid, topk_method noaux_tc, n_group, topk_group, num_experts_per_tok,
+ * norm_topk_prob, routed_scaling_factor).
+ *   s = sigmoid(x W_r^T); sel = s + router_bias (selection only);
+ *   if n_group > 1 only the topk_group groups (contiguous, E/n_group experts)
+ *   with the largest sum-of-two-best sel stay eligible;
+ *   topk_ids = the k largest sel (ties: lower id), written ascending;
+ *   topk_weights = s[ids] / sum(s[ids]) (if norm_topk_prob) * routed_scaling_factor.
+ * x [T][H] act_dtype; router_w [E][H] act_dtype; router_bias [E] fp32;
+ * topk_ids [T][k] int32; topk_weights [T][k] fp32. */
+moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* router_w,
+                       const float* router_bias, int64_t num_tokens, int32_t* topk_ids,
+                       float* topk_weights, void* ws, size_t ws_bytes, void* stream);
+
+/* Grouping of the T*k (token, slot) pairs by expert, stable in token order.
+ *   expert_offsets [E+1]: segment of expert e is [offsets[e], offsets[e+1]),
+ *     offsets[E] = T*k;
+ *   sorted_token_ids [T*k]: token of each grouped row, ascending inside a segment;
+ *   inv_perm [T*k]: inv_perm[t*k+j] = grouped row of (t, j);
+ *   x_perm [T*k][H]: x[sorted_token_ids[p]]; act_dtype, or for FP8 weights the
+ *     e4m3 codes (1 byte each) of the dynamically quantised row, with
+ *   x_perm_scales [T*k][H/128] fp32 (FP8 only, else may be NULL): per token and
+ *     128 channels s = amax/448 (1 if all zero), code = e4m3(RNE, saturating)(x/s)
+ *     ("Kimi K2 . Down projection", quantization_config: activation_scheme dynamic).
+ * x_perm may be NULL (then only the index arrays are produced). */
+moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* topk_ids,
+                         int64_t num_tokens, int32_t* expert_offsets, int32_t* sorted_token_ids,
+                         int32_t* inv_perm, void* x_perm, float* x_perm_scales, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Expert FFNs ("Kimi K2 . Down projection": down_proj(act_fn(gate_proj(x)) *
+ * up_proj(x)), act_fn silu): for every grouped row p of expert e,
+ *   y_perm[p] = W_down[e] (silu(W_gate[e] a_p) * (W_up[e] a_p)), a_p = x_perm[p];
+ * and for every token t the shared expert y_shared[t] = the same form on x[t]
+ * with the shared weights.  FP8: a_p is the dequantised x_perm row; the shared
+ * expert quantises x the same way; the SwiGLU output is quantised again per row
+ * and 128 channels before the down projection; weights are code * block scale.
+ * x [T][H] act_dtype; x_perm/x_perm_scales as produced by moe_permute;
+ * expert_offsets [E+1]; y_perm [T*k][H] act_dtype; y_shared [T][H] act_dtype
+ * (ignored when n_shared_experts == 0). */
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                            const void* x_perm, const float* x_perm_scales,
+                            const int32_t* expert_offsets, int64_t num_tokens, void* y_perm,
+                            void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine with the shared-expert add:
+ *   out[t] = y_shared[t] + sum_{j<k} topk_weights[t][j] * y_perm[inv_perm[t*k+j]],
+ * accumulated in fp32 in slot order, rounded once to act_dtype (nearest even).
+ * y_shared may be NULL when n_shared_experts == 0.  out [T][H] act_dtype. */
+moe_status_t moe_combine(const moe_config_t* cfg, const void* y_perm, const void* y_shared,
+                         const float* topk_weights, const int32_t* inv_perm, int64_t num_tokens,
+                         void* out, void* stream);
+
+/* The whole layer: route -> group -> expert FFNs (rows gathered on the fly,
+ * nothing materialised per row beyond the SwiGLU output) -> combine.
+ * out [T][H] act_dtype.  topk_ids_out [T][k] int32 and topk_weights_out
+ * [T][k] fp32 are optional (NULL: kept in the workspace). */
+moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                               const void* router_w, const float* router_bias, int64_t num_tokens,
+                               void* out, int32_t* topk_ids_out, float* topk_weights_out,
+                               void* ws, size_t ws_bytes, void* stream);
+
+const char* moe_status_string(moe_status_t status);
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+int moe_abi_version(void);
+
+/* Profiling aid.  Arms a one-shot pair of HIP events (hipEvent_t passed as
+ * void*) that the next launch of kernel `kernel_id` (MOE_KID_*) on any
+ * stream records around itself; NULL/NULL disarms.  Host-side state shared by
+ * all threads: only for single-threaded benchmarking. */
+enum {
+  MOE_KID_ROUTER_LOGITS = 0, /* x W_r^T                                        */
+  MOE_KID_ROUTER_TOPK = 1,   /* sigmoid, bias, groups, top-k, weights          */
+  MOE_KID_PERMUTE = 2,       /* histogram + scan + stable scatter (3 kernels)  */
+  MOE_KID_TILES = 3,         /* work list of the grouped GEMMs                 */
+  MOE_KID_GATHER = 4,        /* x_perm rows (moe_permute only)                 */
+  MOE_KID_ACT_QUANT = 5,     /* fp8 activation quantisation of x               */
+  MOE_KID_GATE_UP = 6,       /* grouped gate/up GEMM + SiLU * up               */
+  MOE_KID_DOWN = 7,          /* grouped down GEMM                              */
+  MOE_KID_COMBINE = 8,       /* weighted combine + shared add                  */
+  MOE_KID_COUNT = 9
+};
+moe_status_t moe_profile_arm(int32_t kernel_id, void* ev_start, void* ev_stop);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,81 @@
+// Weighted combine fused with the shared-expert add:
+//   out[t] = y_shared[t] + sum_j w[t][j] * y[inv[t*k + j]]
+// (norm_topk_prob / routed_scaling_factor are already in w; the shared expert
+// has weight 1 -- "Kimi K2 Base" raw config fields: n_shared_experts 1).
+// fp32 accumulation in slot order, one rounding at the end; one block per
+// token, 16-byte vectors.
+#include "kernels.h"
+
+namespace moe {
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
+  __shared__ float ws[32];
+  __shared__ int64_t rs[32];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < a.k) {
+    ws[threadIdx.x] = a.w[t * a.k + threadIdx.x];
+    rs[threadIdx.x] = a.inv[t * a.k + threadIdx.x];
+  }
+  __syncthreads();
+  constexpr int VEC = BF16 ? 8 : 4;
+  const int nv = a.H / VEC;
+  for (int c = threadIdx.x; c < nv; c += blockDim.x) {
+    float acc[VEC];
+    if (BF16) {
+      const uint16_t* ysh = static_cast<const uint16_t*>(a.y_sh);
+      const uint16_t* y = static_cast<const uint16_t*>(a.y);
+      if (ysh) {
+        uint4 v = reinterpret_cast<const uint4*>(ysh + t * a.H)[c];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = bf16_to_f32(static_cast<uint16_t>(w4[i] & 0xffffu));
+          acc[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w4[i] >> 16));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+      }
+      for (int j = 0; j < a.k; ++j) {
+        uint4 v = reinterpret_cast<const uint4*>(y + rs[j] * a.H)[c];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        const float wj = ws[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(w4[i] & 0xffffu)), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(w4[i] >> 16)), acc[2 * i + 1]);
+        }
+      }
+      uint4 o;
+      uint32_t* op = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        op[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
+                (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+      reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + t * a.H)[c] = o;
+    } else {
+      const float* ysh = static_cast<const float*>(a.y_sh);
+      const float* y = static_cast<const float*>(a.y);
+      float4 s = ysh ? reinterpret_cast<const float4*>(ysh + t * a.H)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      acc[0] = s.x; acc[1] = s.y; acc[2] = s.z; acc[3] = s.w;
+      for (int j = 0; j < a.k; ++j) {
+        float4 v = reinterpret_cast<const float4*>(y + rs[j] * a.H)[c];
+        const float wj = ws[j];
+        acc[0] = fmaf(wj, v.x, acc[0]); acc[1] = fmaf(wj, v.y, acc[1]);
+        acc[2] = fmaf(wj, v.z, acc[2]); acc[3] = fmaf(wj, v.w, acc[3]);
+      }
+      reinterpret_cast<float4*>(static_cast<float*>(a.out) + t * a.H)[c] =
+          make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+}
+
+hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t st) {
+  const int threads = 256;
+  if (bf16) hipLaunchKernelGGL(combine_rows<true>, dim3(a.T), dim3(threads), 0, st, a);
+  else hipLaunchKernelGGL(combine_rows<false>, dim3(a.T), dim3(threads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,84 @@
+// Device helpers shared by the HIP kernels of libmoe (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+constexpr int kWave = 64;
+
+// ---- bf16 <-> fp32 -------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// round to nearest even; NaN stays NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// element access for the two activation dtypes
+template <typename T> struct Act;
+template <> struct Act<float> {
+  static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Act<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// ---- e4m3fn (OCP fp8: 1-4-3, bias 7, max 448, no inf) ---------------------
+// Round to nearest, ties to even, saturating at +-448.  |v| below 2^-6 uses
+// the subnormal spacing 2^-9; the code of a normal value is
+// ((e + 6) << 3) + m with m = rint(|v| * 2^(3-e)) in [8, 16], which carries a
+// mantissa overflow into the exponent field by itself.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fabsf(v);
+  uint32_t code;
+  if (!(a < 448.0f)) {
+    code = 0x7eu;  // saturate (also NaN -> 448: inputs are finite by construction)
+  } else if (a < 0.015625f) {
+    code = static_cast<uint32_t>(rintf(a * 512.0f));  // 0..8; 8 is the smallest normal
+  } else {
+    int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;  // -6..8
+    float m = rintf(a * __uint_as_float(static_cast<uint32_t>(127 + 3 - e) << 23));
+    code = static_cast<uint32_t>((e + 6) << 3) + static_cast<uint32_t>(m);
+  }
+  return static_cast<uint8_t>(code | sign);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---- grouped-GEMM work list ----------------------------------------------
+// One entry per (group, tile of up to BM grouped rows).  Groups 0..E-1 are the
+// routed experts (rows [offsets[e], offsets[e+1]) of the grouped order), group
+// E is the shared expert (rows T*k + t for token t).
+struct Tile {
+  int32_t group;
+  int32_t row0;   // first grouped row of the tile
+  int32_t rows;   // 1..BM
+  int32_t pad;
+};
+
+}  // namespace moe

@@ -1,0 +1,264 @@
+// Grouped expert FFN, weight-streaming schedule (few rows per expert, the
+// memory-bound decode regime: "MoE GEMMs remain memory-bound" -- "Behind
+// Kimi-K2's Config", section 2.1, Decode bullet).
+//
+// Expert form ("Kimi K2 . Down projection"): y = W_down (silu(W_gate a) *
+// (W_up a)), weights [out][in].
+//
+// Layout of the work: the output is computed transposed, Y^T = W A^T, so the
+// long weight dimension is the MFMA M side and up to 16 grouped rows (tokens)
+// form N.  A block is 4 waves that split the K loop of one 16-row (gate_up:
+// 16 gate + 16 up rows) or 32-row (down) weight slab; every lane streams 64
+// contiguous bytes of one weight row per K step of 128 (16x16x32 bf16 MFMA,
+// the K order inside a step permuted the same way for both operands), so each
+// weight byte is read exactly once per tile of 16 rows.  The four partial sums
+// meet in LDS in a fixed order (deterministic).  Grid: x = weight slab, y =
+// work-list tile; tiles past the device-side count exit at once.
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kWK = 4;  // waves splitting K
+
+template <int NA>
+struct Frag {
+  uint4 a[NA][4];
+  uint4 b[4];
+};
+
+template <int NA>
+__device__ __forceinline__ void load_frag(Frag<NA>& f, const uint16_t* const (&pa)[NA],
+                                          const uint16_t* pb, int koff) {
+#pragma unroll
+  for (int m = 0; m < NA; ++m) {
+    const uint4* s = reinterpret_cast<const uint4*>(pa[m] + koff);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[m][i] = s[i];
+  }
+  const uint4* s = reinterpret_cast<const uint4*>(pb + koff);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.b[i] = s[i];
+}
+
+template <int NA>
+__device__ __forceinline__ void mma_frag(const Frag<NA>& f, f32x4 (&acc)[NA]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 0; m < NA; ++m)
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.a[m][i]),
+                                                       __builtin_bit_cast(bf16x8, f.b[i]), acc[m],
+                                                       0, 0, 0);
+}
+
+// K loop of one wave over steps wave, wave+kWK, ... (double-buffered loads),
+// then the kWK partial sums are added in LDS; wave 0 returns the total.
+template <int NA>
+__device__ __forceinline__ void stream_k(const uint16_t* const (&pa)[NA], const uint16_t* pb,
+                                         int steps, f32x4 (&acc)[NA]) {
+  __shared__ f32x4 red[kWK - 1][NA][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 0; m < NA; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int s = wave;
+  Frag<NA> cur, nxt;
+  if (s < steps) load_frag<NA>(cur, pa, pb, s * 128);
+  while (s < steps) {
+    const int sn = s + kWK;
+    if (sn < steps) load_frag<NA>(nxt, pa, pb, sn * 128);
+    mma_frag<NA>(cur, acc);
+    cur = nxt;
+    s = sn;
+  }
+  if (wave > 0)
+#pragma unroll
+    for (int m = 0; m < NA; ++m) red[wave - 1][m][lane] = acc[m];
+  __syncthreads();
+  if (wave == 0)
+#pragma unroll
+    for (int w = 0; w < kWK - 1; ++w)
+#pragma unroll
+      for (int m = 0; m < NA; ++m) acc[m] += red[w][m][lane];
+}
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  v.y = static_cast<uint32_t>(f32_to_bf16(c)) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16);
+  *reinterpret_cast<uint2*>(dst) = v;
+}
+
+}  // namespace
+
+// gate_up: block = 16 intermediate features of one tile
+__global__ __launch_bounds__(256) void gate_up_stream_bf16(FfnArgs a) {
+  const int ti = blockIdx.y;
+  if (ti >= *a.tile_count) return;
+  const Tile tl = a.tiles[ti];
+  const bool sh = tl.group == a.E;
+  const int Fg = sh ? a.Fs : a.F;
+  const int f0 = blockIdx.x * 16;
+  if (f0 >= Fg) return;
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int64_t H = a.H, TK = static_cast<int64_t>(a.T) * a.k;
+  const uint16_t* wg = static_cast<const uint16_t*>(sh ? a.sh_gate : a.w_gate);
+  const uint16_t* wu = static_cast<const uint16_t*>(sh ? a.sh_up : a.w_up);
+  const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.F * H;
+  const uint16_t* pa[2] = {wg + wofs + (f0 + r) * H + q * 32, wu + wofs + (f0 + r) * H + q * 32};
+  const int64_t p = tl.row0 + min(r, tl.rows - 1);
+  const uint16_t* pb;
+  if (sh) pb = static_cast<const uint16_t*>(a.xs) + (p - TK) * H;
+  else pb = static_cast<const uint16_t*>(a.xr) + (a.xr_rows ? a.xr_rows[p] : p) * H;
+  pb += q * 32;
+  f32x4 acc[2];
+  stream_k<2>(pa, pb, a.H / 128, acc);
+  if ((threadIdx.x >> 6) == 0 && r < tl.rows) {
+    const int64_t pr = tl.row0 + r;
+    uint16_t* dst = sh ? static_cast<uint16_t*>(a.h_sh) + (pr - TK) * a.Fs
+                       : static_cast<uint16_t*>(a.h) + pr * a.F;
+    store_bf16x4(dst + f0 + 4 * q, silu(acc[0][0]) * acc[1][0], silu(acc[0][1]) * acc[1][1],
+                 silu(acc[0][2]) * acc[1][2], silu(acc[0][3]) * acc[1][3]);
+  }
+}
+
+// down: block = 32 hidden outputs of one tile
+__global__ __launch_bounds__(256) void down_stream_bf16(FfnArgs a) {
+  const int ti = blockIdx.y;
+  if (ti >= *a.tile_count) return;
+  const Tile tl = a.tiles[ti];
+  const bool sh = tl.group == a.E;
+  const int Fg = sh ? a.Fs : a.F;
+  const int h0 = blockIdx.x * 32;
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int64_t TK = static_cast<int64_t>(a.T) * a.k;
+  const uint16_t* wd = static_cast<const uint16_t*>(sh ? a.sh_down : a.w_down);
+  const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.H * a.F;
+  const uint16_t* pa[2] = {wd + wofs + static_cast<int64_t>(h0 + r) * Fg + q * 32,
+                           wd + wofs + static_cast<int64_t>(h0 + 16 + r) * Fg + q * 32};
+  const int64_t p = tl.row0 + min(r, tl.rows - 1);
+  const uint16_t* pb = sh ? static_cast<const uint16_t*>(a.h_sh) + (p - TK) * a.Fs
+                          : static_cast<const uint16_t*>(a.h) + p * a.F;
+  pb += q * 32;
+  f32x4 acc[2];
+  stream_k<2>(pa, pb, Fg / 128, acc);
+  if ((threadIdx.x >> 6) == 0 && r < tl.rows) {
+    const int64_t pr = tl.row0 + r;
+    uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (pr - TK) * a.H
+                       : static_cast<uint16_t*>(a.y) + pr * a.H;
+    store_bf16x4(dst + h0 + 4 * q, acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+    store_bf16x4(dst + h0 + 16 + 4 * q, acc[1][0], acc[1][1], acc[1][2], acc[1][3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: plain FMA, one thread per output element, the input row staged
+// in LDS.  Grid: x = 256 outputs, y = grouped row.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int find_group(const int32_t* offsets, int E, int64_t p) {
+  int lo = 0, hi = E;  // offsets[lo] <= p < offsets[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void gate_up_simple_f32(FfnArgs a) {
+  extern __shared__ float row[];
+  const int64_t p = blockIdx.y;
+  const int64_t TK = static_cast<int64_t>(a.T) * a.k;
+  const bool sh = p >= TK;
+  const int H = a.H, Fg = sh ? a.Fs : a.F;
+  const float* src = sh ? static_cast<const float*>(a.xs) + (p - TK) * H
+                        : static_cast<const float*>(a.xr) + (a.xr_rows ? a.xr_rows[p] : p) * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) row[i] = src[i];
+  __syncthreads();
+  const int f = blockIdx.x * blockDim.x + threadIdx.x;
+  if (f >= Fg) return;
+  const int e = sh ? 0 : find_group(a.offsets, a.E, p);
+  const float* wg = sh ? static_cast<const float*>(a.sh_gate)
+                       : static_cast<const float*>(a.w_gate) + static_cast<int64_t>(e) * a.F * H;
+  const float* wu = sh ? static_cast<const float*>(a.sh_up)
+                       : static_cast<const float*>(a.w_up) + static_cast<int64_t>(e) * a.F * H;
+  wg += static_cast<int64_t>(f) * H;
+  wu += static_cast<int64_t>(f) * H;
+  float g = 0.f, u = 0.f;
+  for (int i = 0; i < H; ++i) {
+    g = fmaf(row[i], wg[i], g);
+    u = fmaf(row[i], wu[i], u);
+  }
+  float* dst = sh ? static_cast<float*>(a.h_sh) + (p - TK) * a.Fs : static_cast<float*>(a.h) + p * a.F;
+  dst[f] = g / (1.0f + expf(-g)) * u;
+}
+
+__global__ __launch_bounds__(256) void down_simple_f32(FfnArgs a) {
+  extern __shared__ float row[];
+  const int64_t p = blockIdx.y;
+  const int64_t TK = static_cast<int64_t>(a.T) * a.k;
+  const bool sh = p >= TK;
+  const int H = a.H, Fg = sh ? a.Fs : a.F;
+  const float* src = sh ? static_cast<const float*>(a.h_sh) + (p - TK) * a.Fs
+                        : static_cast<const float*>(a.h) + p * a.F;
+  for (int i = threadIdx.x; i < Fg; i += blockDim.x) row[i] = src[i];
+  __syncthreads();
+  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= H) return;
+  const int e = sh ? 0 : find_group(a.offsets, a.E, p);
+  const float* wd = sh ? static_cast<const float*>(a.sh_down)
+                       : static_cast<const float*>(a.w_down) + static_cast<int64_t>(e) * H * a.F;
+  wd += static_cast<int64_t>(o) * Fg;
+  float y = 0.f;
+  for (int i = 0; i < Fg; ++i) y = fmaf(row[i], wd[i], y);
+  float* dst = sh ? static_cast<float*>(a.y_sh) + (p - TK) * H : static_cast<float*>(a.y) + p * H;
+  dst[o] = y;
+}
+
+hipError_t launch_gate_up_stream(const FfnArgs& a, hipStream_t st) {
+  dim3 grid(std::max(a.F, a.Fs) / 16, static_cast<unsigned>(a.tile_bound));
+  hipLaunchKernelGGL(gate_up_stream_bf16, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_stream(const FfnArgs& a, hipStream_t st) {
+  dim3 grid(a.H / 32, static_cast<unsigned>(a.tile_bound));
+  hipLaunchKernelGGL(down_stream_bf16, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_simple_f32(const FfnArgs& a, bool gate_up, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(a.T) * a.k + (a.Fs > 0 ? a.T : 0);
+  if (gate_up) {
+    dim3 grid((std::max(a.F, a.Fs) + 255) / 256, static_cast<unsigned>(rows));
+    hipLaunchKernelGGL(gate_up_simple_f32, grid, dim3(256), a.H * sizeof(float), st, a);
+  } else {
+    dim3 grid((a.H + 255) / 256, static_cast<unsigned>(rows));
+    hipLaunchKernelGGL(down_simple_f32, grid, dim3(256), std::max(a.F, a.Fs) * sizeof(float), st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// rows per work-list tile for the kernel a call will use
+int ffn_tile_rows(int64_t T, int k, int E, int weight_dtype, int act_dtype) {
+  (void)T; (void)k; (void)E; (void)weight_dtype; (void)act_dtype;
+  return 16;
+}
+
+hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {
+  if (act_dtype == MOE_F32) return launch_simple_f32(a, true, st);
+  if (weight_dtype == MOE_BF16) return launch_gate_up_stream(a, st);
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_down(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {
+  if (act_dtype == MOE_F32) return launch_simple_f32(a, false, st);
+  if (weight_dtype == MOE_BF16) return launch_down_stream(a, st);
+  return hipErrorNotSupported;
+}
+
+}  // namespace moe

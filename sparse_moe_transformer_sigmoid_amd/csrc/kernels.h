@@ -1,0 +1,95 @@
+// Launch interfaces of the libmoe kernels (host side of each .hip file).
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+constexpr int kPermChunk = 256;  // tokens per block in the grouping kernels
+
+struct RouterArgs {
+  const void* x;
+  const void* wr;
+  const float* bias;
+  int T, E, H, k, n_group, topk_group, norm;
+  float scale;
+  bool bf16;
+  float* logits;  // [T][E] scratch
+  int32_t* ids;   // [T][k]
+  float* w;       // [T][k]
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t st);
+hipError_t launch_topk(const RouterArgs& a, hipStream_t st);
+
+struct PermArgs {
+  const int32_t* ids;  // [T][k]
+  int T, k, E;
+  int32_t* chunk_counts;  // [nchunk][E] scratch
+  int32_t* chunk_base;    // [nchunk][E] scratch
+  int32_t* offsets;       // [E+1]
+  int32_t* sorted;        // [T*k] (+T identity rows when identity_tail)
+  int32_t* inv;           // [T*k]
+  bool identity_tail;
+};
+hipError_t launch_permute(const PermArgs& a, hipStream_t st);
+
+struct TileArgs {
+  const int32_t* offsets;  // [E+1]
+  int T, k, E, bm;
+  bool shared;             // append the shared group (rows T*k + t)
+  Tile* tiles;
+  int32_t* tile_count;
+};
+// upper bound on the number of tiles for T tokens (grid size of the GEMMs)
+int64_t max_tiles(int64_t T, int k, int E, bool shared, int bm);
+hipError_t launch_build_tiles(const TileArgs& a, hipStream_t st);
+
+// gather rows: dst[p] = src[rows[p]] for p < n, row_bytes per row (multiple of 16)
+hipError_t launch_gather(const void* src, const int32_t* rows, int64_t n, int64_t row_bytes,
+                         void* dst, hipStream_t st);
+
+// dynamic fp8 quantisation of bf16 rows: codes [R][C] e4m3, scales [R][C/128]
+hipError_t launch_act_quant(const uint16_t* src, int64_t R, int C, uint8_t* codes, float* scales,
+                            hipStream_t st);
+
+// grouped expert FFN
+struct FfnArgs {
+  int T, k, E, H, F, Fs;
+  const Tile* tiles;
+  const int32_t* tile_count;
+  int64_t tile_bound;  // grid size along tiles
+  int bm;              // rows per tile used to build `tiles`
+  const int32_t* offsets;  // [E+1] (simple fp32 kernels)
+  // weights (dtype per mode); routed [E][F][H] / [E][H][F], shared [Fs][H] / [H][Fs]
+  const void *w_gate, *w_up, *w_down, *sh_gate, *sh_up, *sh_down;
+  const float *s_gate, *s_up, *s_down, *sh_s_gate, *sh_s_up, *sh_s_down;
+  // gate/up input rows: routed grouped row p reads xr[xr_rows ? xr_rows[p] : p],
+  // shared row T*k+t reads xs[t]; fp8 carries per-128 scales alongside
+  const void* xr;
+  const float* xr_scales;
+  const int32_t* xr_rows;
+  const void* xs;
+  const float* xs_scales;
+  // SwiGLU output: routed [T*k][F], shared [T][Fs] (bf16 / f32 / e4m3 codes)
+  void* h;
+  void* h_sh;
+  float* h_scales;     // fp8: [T*k][F/128]
+  float* h_sh_scales;  // fp8: [T][Fs/128]
+  // down output: routed [T*k][H], shared [T][H] (act dtype)
+  void* y;
+  void* y_sh;
+};
+hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st);
+hipError_t launch_down(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st);
+int ffn_tile_rows(int64_t T, int k, int E, int weight_dtype, int act_dtype);
+
+struct CombineArgs {
+  const void* y;
+  const void* y_sh;
+  const float* w;
+  const int32_t* inv;
+  int T, k, H;
+  void* out;
+};
+hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,223 @@
+// Grouping of (token, slot) pairs by expert: per-chunk histograms (LDS
+// atomics), a per-expert scan over chunks plus an exclusive scan over experts,
+// and a stable scatter.  Stability comes from 64-bit token masks: for a run
+// of 64 tokens every pair ORs its token bit into its expert's LDS mask (OR is
+// order-independent), and its row is the expert's running base plus the
+// number of lower token bits set -- no dependence on atomic arrival order, so
+// the result is the same bit for bit on every run.
+#include "kernels.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int T, int k,
+                                                  int E, int32_t* __restrict__ chunk_counts) {
+  extern __shared__ int32_t cnt[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kPermChunk;
+  const int64_t n = min(static_cast<int64_t>(kPermChunk), T - t0) * k;
+  const int32_t* p = ids + t0 * k;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&cnt[p[i]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    chunk_counts[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+}
+
+// exclusive block scan of one value per thread (blockDim.x <= 1024)
+__device__ int block_exclusive_scan(int v, int* total) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  int inc = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int s = wsum[w];
+    if (w < wave) base += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return base + inc - v;
+}
+
+// one block of 1024 threads; thread e owns expert e (E <= 1024)
+__global__ __launch_bounds__(1024) void perm_scan(const int32_t* __restrict__ chunk_counts,
+                                                  int nchunk, int E, int64_t total_rows,
+                                                  int32_t* __restrict__ chunk_base,
+                                                  int32_t* __restrict__ offsets) {
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E)
+    for (int c = 0; c < nchunk; ++c) {
+      const int64_t i = static_cast<int64_t>(c) * E + e;
+      const int v = chunk_counts[i];
+      chunk_base[i] = run;
+      run += v;
+    }
+  int all;
+  const int off = block_exclusive_scan(e < E ? run : 0, &all);
+  if (e < E) {
+    offsets[e] = off;
+    for (int c = 0; c < nchunk; ++c) chunk_base[static_cast<int64_t>(c) * E + e] += off;
+  }
+  if (e == 0) offsets[E] = static_cast<int32_t>(total_rows);
+}
+
+__global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ ids, int T, int k,
+                                                    int E, const int32_t* __restrict__ chunk_base,
+                                                    int32_t* __restrict__ sorted,
+                                                    int32_t* __restrict__ inv, int identity_tail) {
+  extern __shared__ unsigned long long smem[];
+  unsigned long long* mask = smem;                            // [E]
+  int32_t* run = reinterpret_cast<int32_t*>(smem + E);        // [E]
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    run[e] = chunk_base[static_cast<int64_t>(blockIdx.x) * E + e];
+  const int t_begin = blockIdx.x * kPermChunk;
+  const int t_end = min(t_begin + kPermChunk, T);
+  for (int g0 = t_begin; g0 < t_end; g0 += 64) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
+    __syncthreads();
+    const int n = min(64, t_end - g0) * k;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const int tl = i / k;
+      const int e = ids[static_cast<int64_t>(g0) * k + i];
+      atomicOr(&mask[e], 1ull << tl);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const int tl = i / k;
+      const int64_t flat = static_cast<int64_t>(g0) * k + i;
+      const int e = ids[flat];
+      const int pos = run[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
+      sorted[pos] = g0 + tl;
+      inv[flat] = pos;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) run[e] += __popcll(mask[e]);
+    __syncthreads();
+  }
+  if (identity_tail)
+    for (int t = t_begin + threadIdx.x; t < t_end; t += blockDim.x)
+      sorted[static_cast<int64_t>(T) * k + t] = t;
+}
+
+hipError_t launch_permute(const PermArgs& a, hipStream_t st) {
+  const int nchunk = (a.T + kPermChunk - 1) / kPermChunk;
+  hipLaunchKernelGGL(perm_count, dim3(nchunk), dim3(256), a.E * sizeof(int32_t), st, a.ids, a.T,
+                     a.k, a.E, a.chunk_counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, st, a.chunk_counts, nchunk, a.E,
+                     static_cast<int64_t>(a.T) * a.k, a.chunk_base, a.offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(perm_scatter, dim3(nchunk), dim3(256), a.E * (sizeof(unsigned long long) + 4),
+                     st, a.ids, a.T, a.k, a.E, a.chunk_base, a.sorted, a.inv,
+                     a.identity_tail ? 1 : 0);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// work list of the grouped GEMMs: group g (expert, or the shared expert as
+// group E) contributes ceil(n_g / bm) tiles of consecutive grouped rows.
+// ---------------------------------------------------------------------------
+int64_t max_tiles(int64_t T, int k, int E, bool shared, int bm) {
+  const int64_t rows = T * k;
+  return rows / bm + std::min<int64_t>(E, rows) + (shared ? (T + bm - 1) / bm : 0);
+}
+
+__global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ offsets, int T,
+                                                    int k, int E, int bm, int shared,
+                                                    Tile* __restrict__ tiles,
+                                                    int32_t* __restrict__ tile_count) {
+  const int g = threadIdx.x;  // groups 0..E (E <= 1023)
+  int n = 0, base = 0;
+  if (g < E) {
+    base = offsets[g];
+    n = offsets[g + 1] - base;
+  } else if (g == E && shared) {
+    base = T * k;
+    n = T;
+  }
+  const int nt = (n + bm - 1) / bm;
+  int all;
+  const int start = block_exclusive_scan(nt, &all);
+  for (int i = 0; i < nt; ++i) {
+    Tile t;
+    t.group = g;
+    t.row0 = base + i * bm;
+    t.rows = min(bm, n - i * bm);
+    t.pad = 0;
+    tiles[start + i] = t;
+  }
+  if (g == 0) *tile_count = all;
+}
+
+hipError_t launch_build_tiles(const TileArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(build_tiles, dim3(1), dim3(1024), 0, st, a.offsets, a.T, a.k, a.E, a.bm,
+                     a.shared ? 1 : 0, a.tiles, a.tile_count);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// row gather (16-byte vectors), one block per 4 rows
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gather_rows(const uint4* __restrict__ src,
+                                                   const int32_t* __restrict__ rows, int64_t n,
+                                                   int64_t vec_per_row, uint4* __restrict__ dst) {
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (p >= n) return;
+  const uint4* s = src + static_cast<int64_t>(rows[p]) * vec_per_row;
+  uint4* d = dst + p * vec_per_row;
+  for (int64_t i = threadIdx.x & 63; i < vec_per_row; i += 64) d[i] = s[i];
+}
+
+hipError_t launch_gather(const void* src, const int32_t* rows, int64_t n, int64_t row_bytes,
+                         void* dst, hipStream_t st) {
+  hipLaunchKernelGGL(gather_rows, dim3((n + 3) / 4), dim3(256), 0, st,
+                     static_cast<const uint4*>(src), rows, n, row_bytes / 16,
+                     static_cast<uint4*>(dst));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// dynamic activation quantisation ("Kimi K2 . Down projection", config.json
+// quantization_config: fmt e4m3, activation_scheme dynamic): per row and 128
+// channels s = amax / 448 (1 when the group is all zero), code = e4m3(v / s).
+// One wave per group of 128: two values per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void act_quant_bf16(const uint16_t* __restrict__ src, int64_t R,
+                                                      int C, uint8_t* __restrict__ codes,
+                                                      float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int groups = C / 128;
+  const int64_t gi = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (gi >= R * groups) return;
+  const int64_t row = gi / groups;
+  const int g = static_cast<int>(gi - row * groups);
+  const uint16_t* p = src + row * C + g * 128 + 2 * lane;
+  const uint32_t pair = *reinterpret_cast<const uint32_t*>(p);
+  const float v0 = bf16_to_f32(static_cast<uint16_t>(pair & 0xffffu));
+  const float v1 = bf16_to_f32(static_cast<uint16_t>(pair >> 16));
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+  const uint16_t c = static_cast<uint16_t>(f32_to_e4m3(v0 / s)) |
+                     (static_cast<uint16_t>(f32_to_e4m3(v1 / s)) << 8);
+  *reinterpret_cast<uint16_t*>(codes + row * C + g * 128 + 2 * lane) = c;
+  if (lane == 0) scales[row * groups + g] = s;
+}
+
+hipError_t launch_act_quant(const uint16_t* src, int64_t R, int C, uint8_t* codes, float* scales,
+                            hipStream_t st) {
+  const int64_t groups = R * (C / 128);
+  hipLaunchKernelGGL(act_quant_bf16, dim3((groups + 3) / 4), dim3(256), 0, st, src, R, C, codes,
+                     scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,209 @@
+// Router: logits = x W_r^T (fp32 accumulate), then per token sigmoid scores,
+// correction-bias selection (noaux_tc), optional group restriction, top-k and
+// renormalised, scaled weights.  Config fields from the "Kimi K2 Base" /
+// "Kimi K2 0905" raw config tables (scoring_func sigmoid, topk_method
+// noaux_tc, n_group, topk_group, num_experts_per_tok, norm_topk_prob,
+// routed_scaling_factor).
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// logits, bf16: one block = 16 tokens x 16 experts, 4 waves split the K loop
+// (K steps of 128 taken round-robin), reduced through LDS in a fixed order.
+// MFMA 16x16x32 bf16 with A = router rows (experts), B = token rows.  Each
+// lane streams 64 contiguous bytes of its row per K step; the K order inside
+// a step is permuted identically for A and B, which a dot product allows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_logits_bf16(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr,
+                                                          int T, int E, int H,
+                                                          float* __restrict__ logits) {
+  __shared__ f32x4 red[3][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int tok = min(t0 + r, T - 1);
+  const uint16_t* pa = wr + static_cast<int64_t>(min(e0 + r, E - 1)) * H + q * 32;
+  const uint16_t* pb = x + static_cast<int64_t>(tok) * H + q * 32;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int steps = H / 128;
+  for (int s = wave; s < steps; s += 4) {
+    const uint4* a4 = reinterpret_cast<const uint4*>(pa + s * 128);
+    const uint4* b4 = reinterpret_cast<const uint4*>(pb + s * 128);
+    uint4 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = a4[i]; b[i] = b4[i]; }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                    __builtin_bit_cast(bf16x8, b[i]), acc, 0, 0, 0);
+  }
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) acc += red[w][lane];
+    // lane holds experts e0 + 4q + i (i = 0..3) of token t0 + r
+    if (t0 + r < T) {
+      float* dst = logits + static_cast<int64_t>(t0 + r) * E;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (e0 + 4 * q + i < E) dst[e0 + 4 * q + i] = acc[i];
+    }
+  }
+}
+
+// fp32 logits: one thread per (token, expert), plain fp32 FMA over H.
+__global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict__ x,
+                                                         const float* __restrict__ wr, int T, int E,
+                                                         int H, float* __restrict__ logits) {
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(T) * E) return;
+  int t = static_cast<int>(i / E), e = static_cast<int>(i % E);
+  const float4* a = reinterpret_cast<const float4*>(x + static_cast<int64_t>(t) * H);
+  const float4* b = reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * H);
+  float s = 0.f;
+  for (int h = 0; h < H / 4; ++h) {
+    float4 u = a[h], v = b[h];
+    s = fmaf(u.x, v.x, s); s = fmaf(u.y, v.y, s); s = fmaf(u.z, v.z, s); s = fmaf(u.w, v.w, s);
+  }
+  logits[i] = s;
+}
+
+// ---------------------------------------------------------------------------
+// top-k: one wave per token, 4 tokens per block.  Lane l holds experts
+// l*V .. l*V+V-1.  Each of the k rounds takes the wave-wide maximum of the
+// remaining eligible sel values (ties: lower expert id) by butterfly shuffles.
+// ---------------------------------------------------------------------------
+template <int V>
+__global__ __launch_bounds__(256) void router_topk(const float* __restrict__ logits,
+                                                   const float* __restrict__ bias, int T, int E,
+                                                   int k, int n_group, int topk_group, int norm,
+                                                   float scale, int32_t* __restrict__ ids_out,
+                                                   float* __restrict__ w_out) {
+  __shared__ float sel_lds[4][64 * V];
+  __shared__ float gsc_lds[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  const bool valid = t < T;
+  const int tt = valid ? t : T - 1;
+  float s[V], sel[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int e = lane * V + i;
+    if (e < E) {
+      const float z = logits[static_cast<int64_t>(tt) * E + e];
+      s[i] = 1.0f / (1.0f + expf(-z));
+      sel[i] = s[i] + bias[e];
+    } else {
+      s[i] = 0.f;
+      sel[i] = -INFINITY;
+    }
+  }
+  if (n_group > 1) {  // block-uniform branch
+    const int gsz = E / n_group;
+#pragma unroll
+    for (int i = 0; i < V; ++i) sel_lds[wave][lane * V + i] = sel[i];
+    __syncthreads();
+    float gscore = -INFINITY;
+    if (lane < n_group) {
+      float b1 = -INFINITY, b2 = -INFINITY;
+      for (int j = 0; j < gsz; ++j) {
+        const float v = sel_lds[wave][lane * gsz + j];
+        if (v > b1) { b2 = b1; b1 = v; } else if (v > b2) { b2 = v; }
+      }
+      gscore = gsz > 1 ? b1 + b2 : b1;
+      gsc_lds[wave][lane] = gscore;
+    }
+    __syncthreads();
+    int keep = 0;
+    if (lane < n_group) {
+      int rank = 0;
+      for (int g = 0; g < n_group; ++g) {
+        const float o = gsc_lds[wave][g];
+        rank += (o > gscore) || (o == gscore && g < lane);
+      }
+      keep = rank < topk_group;
+    }
+    __syncthreads();
+    if (lane < n_group) gsc_lds[wave][lane] = keep ? 1.f : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = lane * V + i;
+      if (e < E && gsc_lds[wave][e / gsz] == 0.f) sel[i] = -INFINITY;
+    }
+  }
+  int my_id = 0;
+  float my_s = 0.f;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (sel[i] > bv) { bv = sel[i]; bi = lane * V + i; }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    const int owner = bi / V, slot = bi - owner * V;
+    float cand = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (i == slot) cand = s[i];
+    const float sw = __shfl(cand, owner, 64);
+    if (lane == owner) {
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+        if (i == slot) sel[i] = -INFINITY;
+    }
+    if (lane == r) { my_id = bi; my_s = sw; }
+  }
+  // ascending ids: rank of my_id among the k chosen
+  int rank = 0;
+  for (int j = 0; j < k; ++j) rank += __shfl(my_id, j, 64) < my_id;
+  const float sum = wave_sum(lane < k ? my_s : 0.f);
+  const float w = norm ? (my_s / sum) * scale : my_s * scale;
+  if (valid && lane < k) {
+    ids_out[static_cast<int64_t>(t) * k + rank] = my_id;
+    w_out[static_cast<int64_t>(t) * k + rank] = w;
+  }
+}
+
+hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
+  if (a.bf16) {
+    dim3 grid((a.E + 15) / 16, (a.T + 15) / 16);
+    hipLaunchKernelGGL(router_logits_bf16, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wr), a.T,
+                       a.E, a.H, a.logits);
+  } else {
+    const int64_t n = static_cast<int64_t>(a.T) * a.E;
+    hipLaunchKernelGGL(router_logits_f32, dim3((n + 255) / 256), dim3(256), 0, st,
+                       static_cast<const float*>(a.x), static_cast<const float*>(a.wr), a.T, a.E,
+                       a.H, a.logits);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return hipSuccess;
+}
+
+hipError_t launch_topk(const RouterArgs& a, hipStream_t st) {
+  dim3 grid((a.T + 3) / 4), block(256);
+  const int V = (a.E + 63) / 64;
+#define MOE_TOPK(VV)                                                                         \
+  hipLaunchKernelGGL(router_topk<VV>, grid, block, 0, st, a.logits, a.bias, a.T, a.E, a.k, \
+                     a.n_group, a.topk_group, a.norm, a.scale, a.ids, a.w)
+  if (V <= 1) MOE_TOPK(1);
+  else if (V <= 2) MOE_TOPK(2);
+  else if (V <= 4) MOE_TOPK(4);
+  else if (V <= 6) MOE_TOPK(6);
+  else if (V <= 8) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+}  // namespace moe

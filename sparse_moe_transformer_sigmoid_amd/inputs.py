@@ -71,7 +71,7 @@ class Workload:
     act_dtype: str = BF16          # x, router weight, output
     weight_dtype: str = BF16       # expert weights
     weight_std: float = 0.02
-    bias: str = "normal"           # "normal" | "zipf" | "zero"
+    bias: str = "normal"           # "normal" | "zipf" | "zero" | "hot"
     bias_std: float = 0.01
     zipf_beta: float = 0.1
     zipf_s: float = 1.1
@@ -166,6 +166,11 @@ def gen_bias(wl: Workload) -> torch.Tensor:
         b = np.zeros(E, np.float32)
     elif wl.bias == "normal":
         b = _rng(wl.seed, TID_BIAS).standard_normal(E, np.float32) * np.float32(wl.bias_std)
+    elif wl.bias == "hot":
+        # two experts (the first and the last) favoured by every token
+        b = _rng(wl.seed, TID_BIAS).standard_normal(E, np.float32) * np.float32(wl.bias_std)
+        b[0] += 5.0
+        b[E - 1] += 5.0
     elif wl.bias == "zipf":
         ranks = _rng(wl.seed, TID_ZIPF_RANK).permutation(E) + 1
         b = (-wl.zipf_s * wl.zipf_beta * np.log(ranks.astype(np.float64))).astype(np.float32)

@@ -1,0 +1,148 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/moe.h declares, and rejects bad arguments on the host before any HIP
+call (so fake device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_moe_transformer_sigmoid_amd import binding as B
+from sparse_moe_transformer_sigmoid_amd import inputs as gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libmoe.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[a-z_ ]+[\s\*]+(moe_[a-z_]+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+              "moe_workspace_size", "moe_status_string", "moe_last_error", "moe_abi_version", "moe_profile_arm"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    lib = B.load()
+    for n in declared_functions():
+        assert hasattr(lib, n)
+    assert lib.moe_abi_version() == 1
+
+
+def test_status_strings():
+    assert B.moe_status_string(B.MOE_OK) == "MOE_OK"
+    assert B.moe_status_string(B.MOE_ERR_WORKSPACE) == "MOE_ERR_WORKSPACE"
+    assert B.moe_status_string(77) == "MOE_ERR_UNKNOWN"
+
+
+def k2cfg(**kw):
+    c = B.MoeConfig.from_fields(gen.WORKLOADS["k2_decode_bf16"].fields())
+    for key, v in kw.items():
+        setattr(c, key, v)
+    return c
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def route(cfg, T=4, ws_bytes=1 << 40, x=FAKE, ws=FAKE * 16):
+    lib = B.load()
+    return lib.moe_route(ctypes.byref(cfg), x, FAKE, FAKE, T, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_workspace_size_grows_with_tokens_and_matches_layout():
+    c = k2cfg()
+    s1, s128, s8192 = (B.moe_workspace_size(c, t) for t in (1, 128, 8192))
+    assert 0 < s1 < s128 < s8192
+    # dominated by the per-row SwiGLU output and down output (bf16)
+    per_row = 8 * (2048 + 7168) * 2 + (2048 + 7168) * 2
+    assert s8192 >= 8192 * per_row
+    assert s8192 < 8192 * per_row * 1.1
+    assert B.moe_workspace_size(k2cfg(hidden_size=100), 4) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("scoring_func", 1, B.MOE_ERR_UNSUPPORTED),
+    ("topk_method", 3, B.MOE_ERR_UNSUPPORTED),
+    ("hidden_size", 7000, B.MOE_ERR_INVALID_ARG),
+    ("moe_intermediate_size", 0, B.MOE_ERR_INVALID_ARG),
+    ("n_routed_experts", 2000, B.MOE_ERR_INVALID_ARG),
+    ("num_experts_per_tok", 0, B.MOE_ERR_INVALID_ARG),
+    ("num_experts_per_tok", 33, B.MOE_ERR_INVALID_ARG),
+    ("n_group", 5, B.MOE_ERR_INVALID_ARG),
+    ("topk_group", 2, B.MOE_ERR_INVALID_ARG),
+    ("act_dtype", B.MOE_F32, B.MOE_ERR_UNSUPPORTED),
+])
+def test_bad_config_is_rejected_before_launch(field, value, status):
+    c = k2cfg(**{field: value})
+    assert route(c) == status
+    assert B.moe_last_error() != ""
+
+
+def test_grouped_k_exceeding_allowed_groups():
+    c = k2cfg(n_routed_experts=256, n_group=8, topk_group=1, num_experts_per_tok=33)
+    assert route(c) == B.MOE_ERR_INVALID_ARG
+    c = k2cfg(n_routed_experts=16, n_group=8, topk_group=2, num_experts_per_tok=8)
+    assert route(c) == B.MOE_ERR_INVALID_ARG  # 2 groups x 2 experts < 8
+
+
+def test_token_count_bounds_and_empty_call():
+    c = k2cfg()
+    assert route(c, T=-1) == B.MOE_ERR_INVALID_ARG
+    assert route(c, T=65537) == B.MOE_ERR_INVALID_ARG
+    assert route(c, T=0, x=None, ws=None, ws_bytes=0) == B.MOE_OK  # no-op, nothing touched
+
+
+def test_null_misaligned_and_small_workspace():
+    c = k2cfg()
+    assert route(c, x=None) == B.MOE_ERR_INVALID_ARG
+    assert "x is NULL" in B.moe_last_error()
+    assert route(c, x=FAKE + 2) == B.MOE_ERR_INVALID_ARG
+    assert "aligned" in B.moe_last_error()
+    assert route(c, ws=FAKE + 16) == B.MOE_ERR_INVALID_ARG
+    need = B.moe_workspace_size(c, 4)
+    assert route(c, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE
+    assert "workspace" in B.moe_last_error()
+
+
+def test_layer_forward_weight_pointers_validated():
+    c = k2cfg()
+    w = B.MoeWeights()
+    lib = B.load()
+    st = lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, FAKE, 4, FAKE, None, None,
+                               FAKE * 16, 1 << 40, None)
+    assert st == B.MOE_ERR_INVALID_ARG and "w_gate" in B.moe_last_error()
+    c8 = B.MoeConfig.from_fields(gen.WORKLOADS["k2_fp8"].fields())
+    for n in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
+        setattr(w, n, FAKE)
+    st = lib.moe_layer_forward(ctypes.byref(c8), ctypes.byref(w), FAKE, FAKE, FAKE, 4, FAKE, None, None,
+                               FAKE * 16, 1 << 40, None)
+    assert st == B.MOE_ERR_INVALID_ARG and "s_gate" in B.moe_last_error()
+    c8.weight_block_size[0] = 64
+    assert route(c8) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_profile_arm_validation():
+    lib = B.load()
+    assert lib.moe_profile_arm(B.MOE_KID_COUNT, None, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_profile_arm(0, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_profile_arm(0, None, None) == B.MOE_OK
+
+
+def test_config_struct_layout_matches_header():
+    # 13 int/float fields + int[2], no padding
+    assert ctypes.sizeof(B.MoeConfig) == 15 * 4
+    assert ctypes.sizeof(B.MoeWeights) == 12 * 8

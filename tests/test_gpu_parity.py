@@ -1,0 +1,167 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Small shapes (several tiles, ragged tails) are compared element by element;
+the full Kimi-K2 shapes are compared on routing/permutation for every token
+and on sampled output rows the oracle computes one by one.  Bars: routing ids
+and grouping bit-exact, routing weights within 1e-6 relative, outputs within
+max-abs-err <= tol * max|ref| (fp32 1e-4, bf16 1e-2, fp8 5e-2).
+"""
+import numpy as np
+import pytest
+import torch
+
+import cases
+import oracle
+from gpu_util import TOL, check_route, rel_err, run_layer, run_stages, say
+from sparse_moe_transformer_sigmoid_amd import binding as B
+from sparse_moe_transformer_sigmoid_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+W = gen.WORKLOADS
+
+
+def small_case(wl, T):
+    say(f"[case] {wl.name} T={T} seed={wl.seed} bias={wl.bias}")
+    return cases.make_case(wl, device="cuda", num_tokens=T)
+
+
+SMALL = [
+    (W["tiny_fp32"], 16), (W["tiny_fp32"], 1), (W["tiny_fp32"], 37),
+    (W["small_bf16"], 1), (W["small_bf16"], 7), (W["small_bf16"], 100), (W["small_bf16"], 300),
+    (W["small_grouped_bf16"], 100),
+    (W["small_bf16"].replace(name="small_bf16_hot", bias="hot"), 300),
+    (W["small_bf16"].replace(name="small_bf16_noshared", n_shared_experts=0), 50),
+    (W["small_bf16"].replace(name="small_bf16_shared2", n_shared_experts=2), 50),
+]
+
+
+@pytest.mark.parametrize("wl,T", SMALL, ids=[f"{w.name}-T{t}" for w, t in SMALL])
+def test_layer_matches_oracle_small(wl, T):
+    case = small_case(wl, T)
+    out, ids, w = run_layer(wl, case)
+    ref, route = cases.oracle_forward(wl, case)
+    check_route(ids, w, route)
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e} (tol {TOL[wl.weight_dtype]})")
+    assert err <= TOL[wl.weight_dtype]
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "small_bf16", "small_grouped_bf16"])
+def test_stages_match_oracle_and_layer(name):
+    wl = W[name]
+    case = small_case(wl, wl.num_tokens)
+    r = run_stages(wl, case)
+    ref, route = cases.oracle_forward(wl, case)
+    check_route(r["ids"], r["w"], route)
+    offsets, sorted_ids, inv = oracle.permute(route.ids, wl.n_routed_experts)
+    assert np.array_equal(r["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(r["sorted"].cpu().numpy(), sorted_ids)
+    assert np.array_equal(r["inv"].cpu().numpy(), inv)
+    # the gathered rows are byte copies of x
+    assert torch.equal(r["x_perm"], case["x"][r["sorted"].long()])
+    assert rel_err(r["out"], ref) <= TOL[wl.weight_dtype]
+    out, _, _ = run_layer(wl, case)
+    assert torch.equal(out, r["out"]), "stage chain and fused layer differ"
+
+
+def test_layer_is_deterministic():
+    wl = W["small_bf16"]
+    case = small_case(wl, 300)
+    a, ia, wa = run_layer(wl, case)
+    b, ib, wb = run_layer(wl, case)
+    assert torch.equal(a, b) and torch.equal(ia, ib) and torch.equal(wa, wb)
+
+
+def test_zero_tokens_is_a_noop():
+    wl = W["small_bf16"]
+    case = small_case(wl, 4)
+    case["x"] = case["x"][:0]
+    out, ids, w = run_layer(wl, case)
+    assert out.shape == (0, wl.hidden_size)
+
+
+def test_zero_input_gives_zero_output():
+    wl = W["small_bf16"]
+    case = small_case(wl, 20)
+    case["x"] = torch.zeros_like(case["x"])
+    out, _, _ = run_layer(wl, case)
+    assert torch.count_nonzero(out) == 0
+
+
+# ---------------------------------------------------------------- full size --
+@pytest.fixture(scope="module")
+def k2_weights():
+    wl = W["k2_decode_bf16"]
+    say("[fixture] generating Kimi-K2 bf16 expert weights on the GPU")
+    w = gen.gen_expert_weights(wl, device="cuda")
+    torch.cuda.synchronize()
+    return w
+
+
+def full_case(wl, weights, T=None, experts=None):
+    T = wl.num_tokens if T is None else T
+    say(f"[case] {wl.name} T={T}")
+    x = gen.gen_x(wl, T)
+    rw, b = gen.gen_router(wl), gen.gen_bias(wl)
+    x = cases.enforce_gap(wl, x, rw, b)
+    d = {"x": x.cuda(), "router_w": rw.cuda(), "router_bias": b.cuda()}
+    for k, v in weights.items():
+        # the DeepSeek-V3-shaped workload uses the first 256 experts: the
+        # generator draws expert e from the same stream for any E, so this is
+        # the tensor it would generate for E = 256
+        d[k] = v[:experts] if (experts is not None and k in ("w_gate", "w_up", "w_down")) else v
+    return d
+
+
+def check_sampled(wl, case, out, tokens):
+    ref, _ = cases.oracle_forward(wl, case, tokens=np.asarray(tokens))
+    err = rel_err(out[torch.as_tensor(tokens, device=out.device)], ref)
+    say(f"  sampled tokens {list(tokens)}: rel err {err:.3e}")
+    assert err <= TOL[wl.weight_dtype]
+
+
+def full_route(wl, case):
+    return oracle.route(cases.to64(case["x"]), cases.to64(case["router_w"]), cases.to64(case["router_bias"]),
+                        **cases.route_kwargs(wl))
+
+
+@pytest.mark.parametrize("T", [128, 1, 8, 512])
+def test_k2_decode_full_size(k2_weights, T):
+    wl = W["k2_decode_bf16"]
+    case = full_case(wl, k2_weights, T)
+    out, ids, w = run_layer(wl, case)
+    route = full_route(wl, case)
+    check_route(ids, w, route)
+    say(f"  active experts {len(np.unique(route.ids))}")
+    check_sampled(wl, case, out, [0, T - 1] if T > 1 else [0])
+
+
+def test_k2_prefill_zipf_full_size(k2_weights):
+    wl = W["k2_prefill_bf16_zipf"]
+    case = full_case(wl, k2_weights)
+    r = run_stages(wl, case)
+    route = full_route(wl, case)
+    check_route(r["ids"], r["w"], route)
+    offsets, sorted_ids, inv = oracle.permute(route.ids, wl.n_routed_experts)
+    assert np.array_equal(r["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(r["sorted"].cpu().numpy(), sorted_ids)
+    assert np.array_equal(r["inv"].cpu().numpy(), inv)
+    counts = np.diff(offsets)
+    say(f"  active {int((counts > 0).sum())} empty {int((counts == 0).sum())} hottest {int(counts.max())}")
+    out, _, _ = run_layer(wl, case)
+    assert torch.equal(out, r["out"])
+    hot = int(np.argmax(counts))
+    t_hot = int(sorted_ids[offsets[hot]])
+    check_sampled(wl, case, out, [0, t_hot, wl.num_tokens - 1])
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 128, 512])
+def test_dsv3_grouped_decode_full_size(k2_weights, T):
+    wl = W["dsv3_decode_bf16"]
+    case = full_case(wl, k2_weights, T, experts=256)
+    out, ids, w = run_layer(wl, case)
+    route = full_route(wl, case)
+    check_route(ids, w, route)
+    if T in (8, 512):
+        check_sampled(wl, case, out, [T - 1])
