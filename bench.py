@@ -40,16 +40,25 @@ class Hip:
     """Raw hipEvent handles (the library records them on its own stream)."""
 
     def __init__(self):
-        self.lib = ctypes.CDLL("libamdhip64.so")
+        # the HIP runtime already mapped into this process (torch's copy, which
+        # libmoe binds to as well); a second copy would not know its handles
+        paths = {ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64.so" in ln}
+        if len(paths) != 1:
+            raise RuntimeError(f"expected exactly one HIP runtime mapped, found {sorted(paths)}")
+        self.lib = ctypes.CDLL(paths.pop())
 
     def event(self) -> int:
         ev = ctypes.c_void_p()
         assert self.lib.hipEventCreate(ctypes.byref(ev)) == 0
         return ev.value
 
-    def elapsed_ms(self, a: int, b: int) -> float:
+    def elapsed_ms(self, a: int, b: int):
+        """Milliseconds between two recorded events, None if either was never
+        recorded (the failed query's sticky error is cleared)."""
         ms = ctypes.c_float()
-        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            self.lib.hipGetLastError()
+            return None
         return ms.value
 
 
@@ -176,9 +185,9 @@ def main():
 
     wl = gen.WORKLOADS[args.workload]
     T = args.tokens or wl.num_tokens
-    hip = Hip()
     B.load()
     case = setup(wl, T)
+    hip = Hip()
     cfg = B.MoeConfig.from_fields(wl.fields())
     weights = B.MoeWeights.from_tensors(case)
     out = torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda")
@@ -202,7 +211,7 @@ def main():
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))
+    gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))  # every step launches it
     ms_per_step = wall * 1e3 / args.steps
 
     detail = {}
@@ -217,10 +226,9 @@ def main():
             step()
             torch.cuda.synchronize()
             for kid, (a, b) in enumerate(pairs):
-                try:
-                    per[names[kid]].append(hip.elapsed_ms(a, b))
-                except AssertionError:
-                    pass
+                ms = hip.elapsed_ms(a, b)
+                if ms is not None:
+                    per[names[kid]].append(ms)
             for kid in range(len(names)):
                 B.moe_profile_arm(kid, None, None)
         detail = {n: round(float(np.median(v)), 4) for n, v in per.items() if v}

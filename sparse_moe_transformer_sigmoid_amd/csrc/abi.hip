@@ -44,6 +44,9 @@ struct Probe {
   }
 };
 
+// hipGetLastError reports the last error of any HIP call on the thread; the
+// entry points clear a stale one before their first launch so that only
+// their own launch failures are reported
 #define MOE_LAUNCH(kid, expr)                                                                \
   do {                                                                                       \
     hipError_t e_;                                                                           \
@@ -338,6 +341,7 @@ moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* route
   NEED(topk_ids);
   NEED(topk_weights);
   TRY(check_ws(cfg, T, ws, ws_bytes));
+  (void)hipGetLastError();
   return run_route(cfg, x, router_w, router_bias, T, topk_ids, topk_weights, ws,
                    static_cast<hipStream_t>(stream));
 }
@@ -359,6 +363,7 @@ moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* 
     if (fp8(cfg)) NEED(x_perm_scales);
   }
   TRY(check_ws(cfg, T, ws, ws_bytes));
+  (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
   TRY(run_permute(cfg, topk_ids, T, expert_offsets, sorted_token_ids, inv_perm, false, ws, st));
   if (!x_perm) return MOE_OK;
@@ -394,6 +399,7 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, const moe_weights_t* w, con
     NEED(y_shared);
   }
   TRY(check_ws(cfg, T, ws, ws_bytes));
+  (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
   FfnArgs f = ffn_args(cfg, T, ws);
   f.offsets = expert_offsets;
@@ -425,6 +431,7 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_perm, const void
   NEED(inv_perm);
   NEED(out);
   if (cfg->n_shared_experts > 0) NEED(y_shared);
+  (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
   CombineArgs a{y_perm, cfg->n_shared_experts > 0 ? y_shared : nullptr, topk_weights, inv_perm,
                 static_cast<int>(T), cfg->num_experts_per_tok, cfg->hidden_size, out};
@@ -448,6 +455,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   if (topk_ids_out && !aligned(topk_ids_out)) return fail(MOE_ERR_INVALID_ARG, "topk_ids_out is not 16-byte aligned");
   if (topk_weights_out && !aligned(topk_weights_out)) return fail(MOE_ERR_INVALID_ARG, "topk_weights_out is not 16-byte aligned");
   TRY(check_ws(cfg, T, ws, ws_bytes));
+  (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Layout L = layout(cfg, T);
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
