@@ -107,14 +107,22 @@ def roofline(wl: gen.Workload, T: int, n_active: int, gate_up_ms: float, traffic
             "kernel": "gate_up", "kernel_ms": round(gate_up_ms, 4), "algorithmic_bytes": bytes_}
 
 
+def source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16] if os.path.exists(p) else ""
+
+
 def stored_traffic(workload: str):
-    """HBM bytes per gate_up launch measured by rocprofv3 counters, if they were
-    taken on the current kernel sources (else None)."""
+    """HBM bytes per gate_up launch measured by rocprofv3 counters (FETCH_SIZE +
+    WRITE_SIZE scaled by a 1 GiB copy), if they were taken on the current
+    sources of that kernel (else None)."""
     p = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    return d.get("traffic_bytes") if d.get("kernel_hash") == kernel_hash() else None
+    if any(source_hash(f) != h for f, h in d.get("sources", {}).items()):
+        return None
+    return d.get("traffic_bytes")
 
 
 def cpu_baseline(wl, case, T, budget_s):
