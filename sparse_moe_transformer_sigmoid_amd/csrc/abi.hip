@@ -111,15 +111,16 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0
 // workspace layout (one layout serves every entry point)
 // --------------------------------------------------------------------------
 struct Layout {
-  size_t logits, ids, w, ccount, cbase, offsets, rows, inv, tiles, tcount, xq, xs, h, hs, hsh,
-      hssh, y, ysh, total;
+  size_t logits, ids, w, ccount, cbase, offsets, rows, inv, tiles, tcount, xq, xs, h, hq, hs, hsh,
+      hqsh, hssh, y, ysh, total;
 };
 
 Layout layout(const moe_config_t* c, int64_t T) {
   const int64_t E = c->n_routed_experts, k = c->num_experts_per_tok, H = c->hidden_size;
   const int64_t F = c->moe_intermediate_size, Fs = shared_F(c);
   const int64_t nchunk = (T + kPermChunk - 1) / kPermChunk;
-  const int64_t hsz = fp8(c) ? 1 : act_size(c->act_dtype);
+  // SwiGLU output element: act dtype, or fp32 ahead of its fp8 re-quantisation
+  const int64_t hsz = fp8(c) ? 4 : act_size(c->act_dtype);
   const int64_t asz = act_size(c->act_dtype);
   Layout L{};
   size_t off = 0;
@@ -141,8 +142,10 @@ Layout layout(const moe_config_t* c, int64_t T) {
   L.xq = take(fp8(c) ? T * H : 0);
   L.xs = take(fp8(c) ? T * (H / 128) * 4 : 0);
   L.h = take(T * k * F * hsz);
+  L.hq = take(fp8(c) ? T * k * F : 0);
   L.hs = take(fp8(c) ? T * k * (F / 128) * 4 : 0);
   L.hsh = take(T * Fs * hsz);
+  L.hqsh = take(fp8(c) ? T * Fs : 0);
   L.hssh = take(fp8(c) ? T * (Fs / 128) * 4 : 0);
   L.y = take(T * k * H * asz);
   L.ysh = take(T * H * asz);
@@ -290,6 +293,8 @@ FfnArgs ffn_args(const moe_config_t* c, int64_t T, void* ws) {
   f.Fs = shared_F(c);
   f.h = at<void>(ws, L.h);
   f.h_sh = at<void>(ws, L.hsh);
+  f.hq = at<void>(ws, L.hq);
+  f.hq_sh = at<void>(ws, L.hqsh);
   f.h_scales = at<float>(ws, L.hs);
   f.h_sh_scales = at<float>(ws, L.hssh);
   return f;

@@ -245,19 +245,22 @@ namespace moe {
 
 // rows per work-list tile for the kernel a call will use
 int ffn_tile_rows(int64_t T, int k, int E, int weight_dtype, int act_dtype) {
-  (void)T; (void)k; (void)E; (void)weight_dtype; (void)act_dtype;
+  (void)T; (void)k; (void)E; (void)act_dtype;
+  if (weight_dtype == MOE_FP8_E4M3) return fp8_tile_rows();
   return 16;
 }
 
 hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {
   if (act_dtype == MOE_F32) return launch_simple_f32(a, true, st);
   if (weight_dtype == MOE_BF16) return launch_gate_up_stream(a, st);
+  if (weight_dtype == MOE_FP8_E4M3) return launch_gate_up_fp8(a, st);
   return hipErrorNotSupported;
 }
 
 hipError_t launch_down(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {
   if (act_dtype == MOE_F32) return launch_simple_f32(a, false, st);
   if (weight_dtype == MOE_BF16) return launch_down_stream(a, st);
+  if (weight_dtype == MOE_FP8_E4M3) return launch_down_fp8(a, st);
   return hipErrorNotSupported;
 }
 

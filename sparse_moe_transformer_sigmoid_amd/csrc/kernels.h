@@ -47,9 +47,11 @@ hipError_t launch_build_tiles(const TileArgs& a, hipStream_t st);
 hipError_t launch_gather(const void* src, const int32_t* rows, int64_t n, int64_t row_bytes,
                          void* dst, hipStream_t st);
 
-// dynamic fp8 quantisation of bf16 rows: codes [R][C] e4m3, scales [R][C/128]
+// dynamic fp8 quantisation of bf16 / fp32 rows: codes [R][C] e4m3, scales [R][C/128]
 hipError_t launch_act_quant(const uint16_t* src, int64_t R, int C, uint8_t* codes, float* scales,
                             hipStream_t st);
+hipError_t launch_act_quant_f32(const float* src, int64_t R, int C, uint8_t* codes, float* scales,
+                                hipStream_t st);
 
 // grouped expert FFN
 struct FfnArgs {
@@ -69,9 +71,12 @@ struct FfnArgs {
   const int32_t* xr_rows;
   const void* xs;
   const float* xs_scales;
-  // SwiGLU output: routed [T*k][F], shared [T][Fs] (bf16 / f32 / e4m3 codes)
+  // SwiGLU output: routed [T*k][F], shared [T][Fs] (act dtype; fp32 for fp8
+  // weights, then quantised into hq / hq_sh codes with per-128 scales)
   void* h;
   void* h_sh;
+  void* hq;            // fp8: [T*k][F] e4m3
+  void* hq_sh;         // fp8: [T][Fs] e4m3
   float* h_scales;     // fp8: [T*k][F/128]
   float* h_sh_scales;  // fp8: [T][Fs/128]
   // down output: routed [T*k][H], shared [T][H] (act dtype)
@@ -81,6 +86,13 @@ struct FfnArgs {
 hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st);
 hipError_t launch_down(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st);
 int ffn_tile_rows(int64_t T, int k, int E, int weight_dtype, int act_dtype);
+// per-kernel-family launchers (ffn_stream.hip, ffn_fp8.hip)
+hipError_t launch_gate_up_stream(const FfnArgs& a, hipStream_t st);
+hipError_t launch_down_stream(const FfnArgs& a, hipStream_t st);
+hipError_t launch_simple_f32(const FfnArgs& a, bool gate_up, hipStream_t st);
+hipError_t launch_gate_up_fp8(const FfnArgs& a, hipStream_t st);
+hipError_t launch_down_fp8(const FfnArgs& a, hipStream_t st);
+int fp8_tile_rows();
 
 struct CombineArgs {
   const void* y;

@@ -191,8 +191,20 @@ hipError_t launch_gather(const void* src, const int32_t* rows, int64_t n, int64_
 // channels s = amax / 448 (1 when the group is all zero), code = e4m3(v / s).
 // One wave per group of 128: two values per lane.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void act_quant_bf16(const uint16_t* __restrict__ src, int64_t R,
-                                                      int C, uint8_t* __restrict__ codes,
+__device__ __forceinline__ void load_pair(const uint16_t* p, float& v0, float& v1) {
+  const uint32_t pair = *reinterpret_cast<const uint32_t*>(p);
+  v0 = bf16_to_f32(static_cast<uint16_t>(pair & 0xffffu));
+  v1 = bf16_to_f32(static_cast<uint16_t>(pair >> 16));
+}
+__device__ __forceinline__ void load_pair(const float* p, float& v0, float& v1) {
+  const float2 v = *reinterpret_cast<const float2*>(p);
+  v0 = v.x;
+  v1 = v.y;
+}
+
+template <typename In>
+__global__ __launch_bounds__(256) void act_quant_rows(const In* __restrict__ src, int64_t R, int C,
+                                                      uint8_t* __restrict__ codes,
                                                       float* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int groups = C / 128;
@@ -200,10 +212,8 @@ __global__ __launch_bounds__(256) void act_quant_bf16(const uint16_t* __restrict
   if (gi >= R * groups) return;
   const int64_t row = gi / groups;
   const int g = static_cast<int>(gi - row * groups);
-  const uint16_t* p = src + row * C + g * 128 + 2 * lane;
-  const uint32_t pair = *reinterpret_cast<const uint32_t*>(p);
-  const float v0 = bf16_to_f32(static_cast<uint16_t>(pair & 0xffffu));
-  const float v1 = bf16_to_f32(static_cast<uint16_t>(pair >> 16));
+  float v0, v1;
+  load_pair(src + row * C + g * 128 + 2 * lane, v0, v1);
   const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
   const float s = amax > 0.f ? amax / 448.0f : 1.0f;
   const uint16_t c = static_cast<uint16_t>(f32_to_e4m3(v0 / s)) |
@@ -215,8 +225,17 @@ __global__ __launch_bounds__(256) void act_quant_bf16(const uint16_t* __restrict
 hipError_t launch_act_quant(const uint16_t* src, int64_t R, int C, uint8_t* codes, float* scales,
                             hipStream_t st) {
   const int64_t groups = R * (C / 128);
-  hipLaunchKernelGGL(act_quant_bf16, dim3((groups + 3) / 4), dim3(256), 0, st, src, R, C, codes,
-                     scales);
+  hipLaunchKernelGGL(act_quant_rows<uint16_t>, dim3((groups + 3) / 4), dim3(256), 0, st, src, R, C,
+                     codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_quant_f32(const float* src, int64_t R, int C, uint8_t* codes, float* scales,
+                                hipStream_t st) {
+  const int64_t groups = R * (C / 128);
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(act_quant_rows<float>, dim3((groups + 3) / 4), dim3(256), 0, st, src, R, C,
+                     codes, scales);
   return hipGetLastError();
 }
 

@@ -33,6 +33,9 @@ SMALL = [
     (W["small_bf16"].replace(name="small_bf16_hot", bias="hot"), 300),
     (W["small_bf16"].replace(name="small_bf16_noshared", n_shared_experts=0), 50),
     (W["small_bf16"].replace(name="small_bf16_shared2", n_shared_experts=2), 50),
+    (W["small_fp8"], 1), (W["small_fp8"], 7), (W["small_fp8"], 100), (W["small_fp8"], 300),
+    (W["small_fp8"].replace(name="small_fp8_hot", bias="hot"), 200),
+    (W["small_fp8"].replace(name="small_fp8_noshared", n_shared_experts=0), 50),
 ]
 
 
@@ -47,7 +50,17 @@ def test_layer_matches_oracle_small(wl, T):
     assert err <= TOL[wl.weight_dtype]
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "small_bf16", "small_grouped_bf16"])
+def check_fp8_codes(x: torch.Tensor, sorted_ids: np.ndarray, codes: torch.Tensor, scales: torch.Tensor):
+    """x_perm codes/scales are the oracle's activation quantisation of the
+    gathered rows, bit for bit (same fp32 divide, RNE-saturating e4m3)."""
+    _, q, s = oracle.act_quant(cases.to64(x)[sorted_ids])
+    got_q = oracle.e4m3_decode(codes.cpu().numpy())
+    assert np.array_equal(scales.cpu().numpy(), s), "activation scales differ"
+    bad = np.argwhere(got_q != q)
+    assert len(bad) == 0, f"{len(bad)} activation codes differ, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "small_bf16", "small_grouped_bf16", "small_fp8"])
 def test_stages_match_oracle_and_layer(name):
     wl = W[name]
     case = small_case(wl, wl.num_tokens)
@@ -58,8 +71,11 @@ def test_stages_match_oracle_and_layer(name):
     assert np.array_equal(r["offsets"].cpu().numpy(), offsets)
     assert np.array_equal(r["sorted"].cpu().numpy(), sorted_ids)
     assert np.array_equal(r["inv"].cpu().numpy(), inv)
-    # the gathered rows are byte copies of x
-    assert torch.equal(r["x_perm"], case["x"][r["sorted"].long()])
+    if wl.weight_dtype == gen.FP8:
+        check_fp8_codes(case["x"], sorted_ids, r["x_perm"], r["x_perm_scales"])
+    else:
+        # the gathered rows are byte copies of x
+        assert torch.equal(r["x_perm"], case["x"][r["sorted"].long()])
     assert rel_err(r["out"], ref) <= TOL[wl.weight_dtype]
     out, _, _ = run_layer(wl, case)
     assert torch.equal(out, r["out"]), "stage chain and fused layer differ"
@@ -154,6 +170,35 @@ def test_k2_prefill_zipf_full_size(k2_weights):
     hot = int(np.argmax(counts))
     t_hot = int(sorted_ids[offsets[hot]])
     check_sampled(wl, case, out, [0, t_hot, wl.num_tokens - 1])
+
+
+@pytest.fixture(scope="module")
+def k2_fp8_weights():
+    wl = W["k2_fp8"]
+    say("[fixture] generating Kimi-K2 fp8 expert weights on the GPU")
+    w = gen.gen_expert_weights(wl, device="cuda")
+    torch.cuda.synchronize()
+    return w
+
+
+@pytest.mark.parametrize("T", [4096, 1, 64])
+def test_k2_fp8_full_size(k2_fp8_weights, T):
+    wl = W["k2_fp8"]
+    case = full_case(wl, k2_fp8_weights, T)
+    if T == 4096:
+        r = run_stages(wl, case)
+        route = full_route(wl, case)
+        check_route(r["ids"], r["w"], route)
+        _, sorted_ids, _ = oracle.permute(route.ids, wl.n_routed_experts)
+        assert np.array_equal(r["sorted"].cpu().numpy(), sorted_ids)
+        check_fp8_codes(case["x"], sorted_ids[:4096], r["x_perm"][:4096], r["x_perm_scales"][:4096])
+        out, _, _ = run_layer(wl, case)
+        assert torch.equal(out, r["out"])
+        check_sampled(wl, case, out, [0, 2047, T - 1])
+    else:
+        out, ids, w = run_layer(wl, case)
+        check_route(ids, w, full_route(wl, case))
+        check_sampled(wl, case, out, [0, T - 1] if T > 1 else [0])
 
 
 @pytest.mark.parametrize("T", [1, 8, 32, 128, 512])
