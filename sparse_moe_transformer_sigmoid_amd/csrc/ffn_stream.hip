@@ -244,22 +244,27 @@ hipError_t launch_simple_f32(const FfnArgs& a, bool gate_up, hipStream_t st) {
 namespace moe {
 
 // rows per work-list tile for the kernel a call will use
+// Rows per work-list tile, which also selects the kernel family: the
+// weight-streaming kernels (16 rows) while experts average fewer than 32
+// rows (decode), the LDS-tiled MFMA kernels (128 rows) beyond that.
 int ffn_tile_rows(int64_t T, int k, int E, int weight_dtype, int act_dtype) {
-  (void)T; (void)k; (void)E; (void)act_dtype;
+  if (act_dtype == MOE_F32) return 16;
   if (weight_dtype == MOE_FP8_E4M3) return fp8_tile_rows();
-  return 16;
+  return T * k >= 32LL * E ? tile_rows() : 16;
 }
 
 hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {
   if (act_dtype == MOE_F32) return launch_simple_f32(a, true, st);
-  if (weight_dtype == MOE_BF16) return launch_gate_up_stream(a, st);
+  if (weight_dtype == MOE_BF16)
+    return a.bm == tile_rows() ? launch_gate_up_tile(a, st) : launch_gate_up_stream(a, st);
   if (weight_dtype == MOE_FP8_E4M3) return launch_gate_up_fp8(a, st);
   return hipErrorNotSupported;
 }
 
 hipError_t launch_down(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {
   if (act_dtype == MOE_F32) return launch_simple_f32(a, false, st);
-  if (weight_dtype == MOE_BF16) return launch_down_stream(a, st);
+  if (weight_dtype == MOE_BF16)
+    return a.bm == tile_rows() ? launch_down_tile(a, st) : launch_down_stream(a, st);
   if (weight_dtype == MOE_FP8_E4M3) return launch_down_fp8(a, st);
   return hipErrorNotSupported;
 }
