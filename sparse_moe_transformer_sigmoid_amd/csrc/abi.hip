@@ -249,7 +249,7 @@ moe_status_t run_permute(const moe_config_t* c, const int32_t* ids, int64_t T, i
 moe_status_t run_ffn(const moe_config_t* c, const moe_weights_t* w, FfnArgs& f, int64_t T,
                      void* ws, hipStream_t st) {
   const Layout L = layout(c, T);
-  const int bm = ffn_tile_rows(T, f.k, f.E, c->weight_dtype, c->act_dtype);
+  const int bm = ffn_tile_rows(f, c->weight_dtype, c->act_dtype);
   f.bm = bm;
   f.tiles = at<Tile>(ws, L.tiles);
   f.tile_count = at<int32_t>(ws, L.tcount);

@@ -247,10 +247,11 @@ namespace moe {
 // Rows per work-list tile, which also selects the kernel family: the
 // weight-streaming kernels (16 rows) while experts average fewer than 32
 // rows (decode), the LDS-tiled MFMA kernels (128 rows) beyond that.
-int ffn_tile_rows(int64_t T, int k, int E, int weight_dtype, int act_dtype) {
+int ffn_tile_rows(const FfnArgs& a, int weight_dtype, int act_dtype) {
   if (act_dtype == MOE_F32) return 16;
   if (weight_dtype == MOE_FP8_E4M3) return fp8_tile_rows();
-  return T * k >= 32LL * E ? tile_rows() : 16;
+  const bool many_rows = static_cast<int64_t>(a.T) * a.k >= 32LL * a.E;
+  return many_rows && tile_shapes_ok(a.H, a.F, a.Fs) ? tile_rows() : 16;
 }
 
 hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {

@@ -6,83 +6,110 @@
 // (W_up a)), weights [out][in].
 //
 // Work item = up to 128 grouped rows of one expert (a tile of the work list)
-// x one slab of weight rows.  Still computed transposed (C[weight row][row]),
-// with 32x32x16 bf16 MFMA:
-//  * the 128 grouped rows (gathered on the fly through the row -> token map)
-//    are staged through LDS once per K step of 64 and shared by all waves;
-//  * each wave streams its own 64 weight rows straight from global memory
-//    into registers (nobody else needs them), double-buffered one step ahead;
-//  * gate_up: a wave owns 32 features = 32 gate + 32 up rows, so SiLU * up is
-//    applied on matching accumulators in the epilogue; down: a wave owns 64
-//    output rows.
-// LDS rows are padded to 144 bytes so the 16-byte fragment reads of 8
-// consecutive lanes hit distinct banks.  The slab count per expert is a
-// multiple of 8, so every tile of one weight slab runs on the same XCD (L2).
+// x one slab of 512 weight rows, computed transposed (C[weight row][row])
+// with 32x32x16 bf16 MFMA.  Each wave owns 128 weight rows x all 128 rows,
+// its 128 x 128 accumulator tile filling the AGPR file:
+//  * gate_up: a wave's 128 weight rows are 64 gate + 64 up rows of the same
+//    64 features, so SiLU * up is applied on matching accumulators;
+//  * down: a wave owns 128 output rows.
+// Both operands go global -> LDS by DMA (global_load_lds_dwordx4, no VGPR
+// staging), 64 K-elements (128 B per row) per step, two 80 KB stages (the
+// whole 160 KB LDS).  Rows are unpadded; 16-byte slot = chunk ^ ((row >> 1)
+// & 7), because with 128-byte rows the 64 banks give bank group 8*(row%2) +
+// slot and a 128-bit read serves 16 lanes per cycle, so any 16 consecutive
+// rows land in distinct groups.  A K step: all fragments of the step read
+// from LDS, then the next step's 20 DMA issues interleaved with the 64
+// MFMAs (3 : 1), then wait + barrier.  The grouped rows are gathered by the
+// DMA itself through the row -> token map.
+//
+// XCD-aware order: workgroups are dealt round-robin to the 8 XCDs.  The
+// (slab, tile) pairs are numbered slab-major and cut into 8 contiguous
+// ranges, range i going to the blocks that land on XCD i, so the tiles that
+// share a weight slab run on one XCD and reuse its L2, for any slab count.
 #include "kernels.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kBM = 128;          // grouped rows per work item
-constexpr int kBK = 64;           // K elements per step
-constexpr int kLds = kBK + 8;     // LDS row stride in bf16 elements (144 B)
+constexpr int kBM = 128;                      // grouped rows per work item
+constexpr int kBW = 512;                      // weight rows per slab
+constexpr int kBK = 64;                       // K elements per step
+constexpr int kRowB = 128;                    // bytes per LDS row (kBK bf16)
+constexpr int kStage = (kBW + kBM) * kRowB;   // 80 KB
+constexpr int kSmem = 2 * kStage;
+constexpr int kXcd = 8;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) void* glb_ptr;
 
 __device__ __forceinline__ f32x16 mma32(const uint4& a, const uint4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+// 16 bytes per lane from global memory straight into LDS at l + 16 * lane
+__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds((glb_ptr)(g), (lds_ptr)(l), 16, 0, 0);
+}
 
 }  // namespace
 
-// MODE 0: gate_up (K = H, 4 waves = 128 features per block)
-// MODE 1: down    (K = F or Fs, 2 waves = 128 output rows per block)
-template <int MODE, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void ffn_tile_bf16(FfnArgs a) {
-  constexpr int NT = 64 * WAVES;                 // threads
-  constexpr int CHUNKS = kBM * kBK * 2 / 16;     // 16-byte chunks of one row tile
-  constexpr int CPT = CHUNKS / NT;               // chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kBM * kLds];
-
-  const int ti = blockIdx.y;
-  if (ti >= *a.tile_count) return;
-  const Tile tl = a.tiles[ti];
+// MODE 0: gate_up (K = H, slab = 256 features = 256 gate + 256 up rows)
+// MODE 1: down    (K = F or Fs, slab = 512 output rows)
+template <int MODE>
+__global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // ---- XCD-chunked mapping of this block to (slab, tile) ----
+  const int ntile = *a.tile_count;
+  const int total = slabs * ntile;
+  const int per = (total + kXcd - 1) / kXcd;
+  const int j = blockIdx.x / kXcd;
+  const int v = (blockIdx.x % kXcd) * per + j;
+  if (j >= per || v >= total) return;
+  const int slab = v / ntile;
+  const Tile tl = a.tiles[v - slab * ntile];
   const bool sh = tl.group == a.E;
   const int Fg = sh ? a.Fs : a.F;
   const int64_t TK = static_cast<int64_t>(a.T) * a.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, kh = lane >> 5;
+  // DMA lane geometry: one wave instruction fills 8 LDS rows (1 KB); lane ->
+  // row (lane >> 3) of that group, slot (lane & 7), which must hold global
+  // chunk slot ^ f(row); f changes by 4 between even and odd 8-row groups
+  const int drow = lane >> 3;
+  const int dch[2] = {(lane & 7) ^ ((drow >> 1) & 7), (lane & 7) ^ ((4 + (drow >> 1)) & 7)};
 
-  // ---- weight rows of this wave (A operand, 2 sub-tiles of 32 rows) ----
+  // ---- weight rows of this wave: two 64-row halves ----
   int K, o0;
-  const uint16_t* pw[2];
+  const uint8_t* wb[2];
   if (MODE == 0) {
     K = a.H;
-    o0 = blockIdx.x * (32 * WAVES);
+    o0 = slab * (kBW / 2);
     if (o0 >= Fg) return;
     const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.F * a.H;
     const uint16_t* wg = static_cast<const uint16_t*>(sh ? a.sh_gate : a.w_gate) + wofs;
     const uint16_t* wu = static_cast<const uint16_t*>(sh ? a.sh_up : a.w_up) + wofs;
-    const int64_t row = o0 + 32 * wave + r32;
-    pw[0] = wg + row * K + kh * 32;
-    pw[1] = wu + row * K + kh * 32;
+    const int64_t f = o0 + 64 * wave + drow;
+    wb[0] = reinterpret_cast<const uint8_t*>(wg + f * K);
+    wb[1] = reinterpret_cast<const uint8_t*>(wu + f * K);
   } else {
     K = Fg;
-    o0 = blockIdx.x * (64 * WAVES);
+    o0 = slab * kBW;
     const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.H * a.F;
     const uint16_t* wd = static_cast<const uint16_t*>(sh ? a.sh_down : a.w_down) + wofs;
-    const int64_t row = o0 + 64 * wave + r32;
-    pw[0] = wd + row * K + kh * 32;
-    pw[1] = wd + (row + 32) * K + kh * 32;
+    const int64_t r = o0 + 128 * wave + drow;
+    wb[0] = reinterpret_cast<const uint8_t*>(wd + r * K);
+    wb[1] = reinterpret_cast<const uint8_t*>(wd + (r + 64) * K);
   }
-
-  // ---- grouped-row tile (B operand) staging: source pointers per chunk ----
-  const uint16_t* src[CPT];
-  int ldo[CPT];
+  const int64_t rstride8 = static_cast<int64_t>(8) * K * 2;   // 8 weight rows, bytes
+  // ---- grouped rows of this wave's 4 DMA instructions (LDS rows 32w + 8i + drow) ----
+  const uint8_t* xb[4];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int idx = tid + c * NT;
-    const int tr = idx >> 3, cc = idx & 7;     // row of the tile, 16-byte column
+  for (int i = 0; i < 4; ++i) {
+    const int tr = 32 * wave + 8 * i + drow;
     const int64_t p = tl.row0 + min(tr, tl.rows - 1);
     const uint16_t* base;
     if (MODE == 0) {
@@ -92,61 +119,70 @@ __global__ __launch_bounds__(64 * WAVES) void ffn_tile_bf16(FfnArgs a) {
       base = sh ? static_cast<const uint16_t*>(a.h_sh) + (p - TK) * a.Fs
                 : static_cast<const uint16_t*>(a.h) + p * a.F;
     }
-    src[c] = base + cc * 8;
-    ldo[c] = tr * kLds + cc * 8;
+    xb[i] = reinterpret_cast<const uint8_t*>(base) + dch[i & 1] * 16;
   }
 
-  f32x16 acc[2][4];
+  auto issue = [&](int s, int buf) {
+    uint8_t* st = smem + buf * kStage;
+    const int64_t ko = static_cast<int64_t>(s) * kRowB;
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+    for (int i = 0; i < 8; ++i) {
+      const int64_t o = i * rstride8 + ko + dch[i & 1] * 16;
+      dma16(wb[0] + o, st + (128 * wave + 8 * i) * kRowB);
+      dma16(wb[1] + o, st + (128 * wave + 64 + 8 * i) * kRowB);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(xb[i] + ko, st + (kBW + 32 * wave + 8 * i) * kRowB);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
 
   const int steps = K / kBK;
-  uint4 stage[CPT];
-  uint4 wcur[2][4], wnxt[2][4];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) stage[c] = *reinterpret_cast<const uint4*>(src[c]);
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) *reinterpret_cast<uint4*>(&lds[0][ldo[c]]) = stage[c];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wcur[m][i] = reinterpret_cast<const uint4*>(pw[m])[i];
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-
-  // Straight-line loop body: the prefetch of the last step re-reads that step
-  // (in bounds) and its LDS write lands in the buffer nobody reads any more.
+  const int sw = (r32 >> 1) & 7;                       // row swizzle of this lane's rows
+  const int arow = (128 * wave + r32) * kRowB;
+  const int brow = (kBW + r32) * kRowB;
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
-    {
-      const int ko = min(s + 1, steps - 1) * kBK;
+    const uint8_t* st = smem + buf * kStage;
+    uint4 af[4][4], bf[4][4];
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) stage[c] = *reinterpret_cast<const uint4*>(src[c] + ko);
+    for (int i = 0; i < 4; ++i) {
+      const int slot = ((kh * 4 + i) ^ sw) * 16;
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < 4; ++m) af[i][m] = *reinterpret_cast<const uint4*>(st + arow + 32 * m * kRowB + slot);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wnxt[m][i] = reinterpret_cast<const uint4*>(pw[m] + ko)[i];
+      for (int n = 0; n < 4; ++n) bf[i][n] = *reinterpret_cast<const uint4*>(st + brow + 32 * n * kRowB + slot);
     }
+    // the fragments must be in registers before the DMA is issued (a wait
+    // for LDS reads placed after it would also wait for the DMA)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // unconditional, so it shares a basic block with the MFMAs: the last step
+    // re-loads its own (in-bounds) data into the buffer nobody reads again
+    issue(min(s + 1, steps - 1), buf ^ 1);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const uint4* bp = reinterpret_cast<const uint4*>(&lds[buf][(32 * n + r32) * kLds + kh * 32]);
-      uint4 b[4];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = bp[i];
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int n = 0; n < 4; ++n) acc[m][n] = mma32(af[i][m], bf[i][n], acc[m][n]);
+    // 20 DMA issues spread over the 64 MFMAs: 3 MFMA, 1 memory op, ...
 #pragma unroll
-        for (int m = 0; m < 2; ++m) acc[m][n] = mma32(wcur[m][i], b[i], acc[m][n]);
+    for (int g = 0; g < 20; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) *reinterpret_cast<uint4*>(&lds[buf ^ 1][ldo[c]]) = stage[c];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wcur[m][i] = wnxt[m][i];
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
@@ -160,32 +196,31 @@ __global__ __launch_bounds__(64 * WAVES) void ffn_tile_bf16(FfnArgs a) {
     if (MODE == 0) {
       uint16_t* dst = sh ? static_cast<uint16_t*>(a.h_sh) + (p - TK) * a.Fs
                          : static_cast<uint16_t*>(a.h) + p * a.F;
-      dst += o0 + 32 * wave + 4 * kh;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 v;
-        const float h0 = silu(acc[0][n][4 * g + 0]) * acc[1][n][4 * g + 0];
-        const float h1 = silu(acc[0][n][4 * g + 1]) * acc[1][n][4 * g + 1];
-        const float h2 = silu(acc[0][n][4 * g + 2]) * acc[1][n][4 * g + 2];
-        const float h3 = silu(acc[0][n][4 * g + 3]) * acc[1][n][4 * g + 3];
-        v.x = static_cast<uint32_t>(f32_to_bf16(h0)) | (static_cast<uint32_t>(f32_to_bf16(h1)) << 16);
-        v.y = static_cast<uint32_t>(f32_to_bf16(h2)) | (static_cast<uint32_t>(f32_to_bf16(h3)) << 16);
-        *reinterpret_cast<uint2*>(dst + 8 * g) = v;
-      }
-    } else {
-      uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (p - TK) * a.H
-                         : static_cast<uint16_t*>(a.y) + p * a.H;
       dst += o0 + 64 * wave + 4 * kh;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          uint2 v;
-          v.x = static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 0])) |
-                (static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 1])) << 16);
-          v.y = static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 2])) |
-                (static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 3])) << 16);
-          *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g) = v;
+          float h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = silu(acc[m][n][4 * g + e]) * acc[m + 2][n][4 * g + e];
+          uint2 v2;
+          v2.x = pack_bf16(h[0], h[1]);
+          v2.y = pack_bf16(h[2], h[3]);
+          *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g) = v2;
+        }
+    } else {
+      uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (p - TK) * a.H
+                         : static_cast<uint16_t*>(a.y) + p * a.H;
+      dst += o0 + 128 * wave + 4 * kh;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2 v2;
+          v2.x = pack_bf16(acc[m][n][4 * g + 0], acc[m][n][4 * g + 1]);
+          v2.y = pack_bf16(acc[m][n][4 * g + 2], acc[m][n][4 * g + 3]);
+          *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g) = v2;
         }
     }
   }
@@ -193,16 +228,29 @@ __global__ __launch_bounds__(64 * WAVES) void ffn_tile_bf16(FfnArgs a) {
 
 int tile_rows() { return kBM; }
 
-hipError_t launch_gate_up_tile(const FfnArgs& a, hipStream_t st) {
-  dim3 grid(std::max(a.F, a.Fs) / 128, static_cast<unsigned>(a.tile_bound));
-  hipLaunchKernelGGL((ffn_tile_bf16<0, 4>), grid, dim3(256), 0, st, a);
+// slabs must divide the weight dimensions: F, Fs by 256, H by 512
+bool tile_shapes_ok(int H, int F, int Fs) {
+  return F % (kBW / 2) == 0 && Fs % (kBW / 2) == 0 && H % kBW == 0;
+}
+
+template <int MODE>
+static hipError_t launch_tile(const FfnArgs& a, int slabs, hipStream_t st) {
+  // the 160 KB of LDS exceed the default per-launch limit; raising it once is enough
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&ffn_tile_bf16<MODE>), hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
+  if (attr != hipSuccess) return attr;
+  const int64_t blocks = static_cast<int64_t>(slabs) * a.tile_bound;
+  hipLaunchKernelGGL((ffn_tile_bf16<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256), kSmem, st, a,
+                     slabs);
   return hipGetLastError();
 }
 
+hipError_t launch_gate_up_tile(const FfnArgs& a, hipStream_t st) {
+  return launch_tile<0>(a, std::max(a.F, a.Fs) / (kBW / 2), st);
+}
+
 hipError_t launch_down_tile(const FfnArgs& a, hipStream_t st) {
-  dim3 grid(a.H / 128, static_cast<unsigned>(a.tile_bound));
-  hipLaunchKernelGGL((ffn_tile_bf16<1, 2>), grid, dim3(128), 0, st, a);
-  return hipGetLastError();
+  return launch_tile<1>(a, a.H / kBW, st);
 }
 
 }  // namespace moe

@@ -85,7 +85,8 @@ struct FfnArgs {
 };
 hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st);
 hipError_t launch_down(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st);
-int ffn_tile_rows(int64_t T, int k, int E, int weight_dtype, int act_dtype);
+int ffn_tile_rows(const FfnArgs& a, int weight_dtype, int act_dtype);
+bool tile_shapes_ok(int H, int F, int Fs);
 // per-kernel-family launchers (ffn_stream.hip, ffn_fp8.hip)
 hipError_t launch_gate_up_stream(const FfnArgs& a, hipStream_t st);
 hipError_t launch_down_stream(const FfnArgs& a, hipStream_t st);
