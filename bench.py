@@ -169,6 +169,69 @@ def cpu_baseline(wl, case, T, budget_s):
                       f"fp64 numpy, {dt:.1f} s", "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def make_step(cfg, weights, wl, case, T):
+    """One layer step on pre-allocated buffers (inputs resident in HBM)."""
+    out = torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda")
+    ids = torch.empty((T, wl.num_experts_per_tok), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, wl.num_experts_per_tok), dtype=torch.float32, device="cuda")
+    ws = B.alloc_workspace(cfg, T)
+
+    def step():
+        B.moe_layer_forward(cfg, weights, case["x"], case["router_w"], case["router_bias"], out, ws, ids, wts)
+    return step, ids
+
+
+def measure(cfg, weights, wl, case, T, steps, warmup, hip):
+    """Time `steps` layer steps after `warmup` untimed ones (synchronised on
+    both sides); the gate_up launch of every timed step is bracketed by HIP
+    events the library records on its own stream."""
+    step, ids = make_step(cfg, weights, wl, case, T)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    n_active = int(torch.unique(ids).numel())
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        B.moe_profile_arm(B.MOE_KID_GATE_UP, *evs[i])
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))  # every step launches it
+    return step, wall, gate_up_ms, n_active
+
+
+def layer_bytes(wl, T, n_active):
+    """Algorithmic HBM bytes of one layer step: every active expert's and the
+    shared expert's weights once, the router, x in and out."""
+    F, Fs, H, E = wl.moe_intermediate_size, wl.shared_intermediate_size, wl.hidden_size, wl.n_routed_experts
+    per = weight_bytes_per_expert_gate_up(wl, F) * 3 // 2
+    sh = weight_bytes_per_expert_gate_up(wl, Fs) * 3 // 2 if Fs else 0
+    act = 2 if wl.act_dtype == gen.BF16 else 4
+    return n_active * per + sh + E * H * act + 4 * E + 2 * T * H * act
+
+
+def sweep(args, wl, case, cfg, weights, hip):
+    """Decode sweep over token counts on the same resident weights; one JSON
+    record per point (tokens/s, time per step, active experts, fraction of
+    8 TB/s for the whole layer's algorithmic bytes)."""
+    recs = []
+    for T in [int(t) for t in args.sweep_tokens.split(",")]:
+        c = dict(case)
+        c["x"] = gen.gen_x(wl, T).cuda()
+        _, wall, gu_ms, n_act = measure(cfg, weights, wl, c, T, args.steps, args.warmup, hip)
+        ms = wall * 1e3 / args.steps
+        by = layer_bytes(wl, T, n_act)
+        rec = {"workload": wl.name, "num_tokens": T, "ms_per_step": round(ms, 4),
+               "tokens_per_s": round(T / ms * 1e3, 1), "active_experts": n_act,
+               "layer_bytes": by, "layer_hbm_frac": round(by / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
+               "gate_up_ms": round(gu_ms, 4)}
+        print(f"[sweep] {json.dumps(rec)}", file=sys.stderr)
+        recs.append(rec)
+    return recs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +245,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--extra-out", default=None, help="append a detail JSON line to this file")
+    ap.add_argument("--sweep-tokens", default=None,
+                    help="comma-separated token counts measured after the main line (stderr / --extra-out)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
@@ -198,28 +263,7 @@ def main():
     hip = Hip()
     cfg = B.MoeConfig.from_fields(wl.fields())
     weights = B.MoeWeights.from_tensors(case)
-    out = torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda")
-    ids = torch.empty((T, wl.num_experts_per_tok), dtype=torch.int32, device="cuda")
-    wts = torch.empty((T, wl.num_experts_per_tok), dtype=torch.float32, device="cuda")
-    ws = B.alloc_workspace(cfg, T)
-
-    def step():
-        B.moe_layer_forward(cfg, weights, case["x"], case["router_w"], case["router_bias"], out, ws, ids, wts)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    n_active = int(torch.unique(ids).numel())
-
-    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        B.moe_profile_arm(B.MOE_KID_GATE_UP, *evs[i])
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))  # every step launches it
+    step, wall, gate_up_ms, n_active = measure(cfg, weights, wl, case, T, args.steps, args.warmup, hip)
     ms_per_step = wall * 1e3 / args.steps
 
     detail = {}
@@ -263,9 +307,12 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, case, T, args.cpu_budget)
+    recs = sweep(args, wl, case, cfg, weights, hip) if args.sweep_tokens else []
     if args.extra_out:
         with open(args.extra_out, "a") as f:
             f.write(json.dumps({**res, "breakdown_ms": detail, "kernel_hash": kernel_hash()}) + "\n")
+            for r in recs:
+                f.write(json.dumps({"sweep": r}) + "\n")
     print(json.dumps(res))
 
 

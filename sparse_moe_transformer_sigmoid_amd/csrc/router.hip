@@ -54,6 +54,77 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const uint16_t* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// logits, bf16, many tokens: one block = 128 tokens x 64 experts, both staged
+// through LDS (144-byte padded rows, conflict-free 128-bit reads) one K step
+// of 64 ahead in registers; wave w owns tokens 32w..32w+31 x all 64 experts
+// (two 32x32x16 MFMA tiles, C[expert][token]).  Every router row is read
+// once per 128 tokens instead of once per 16.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_logits_bf16_tile(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ wr,
+                                                               int T, int E, int H,
+                                                               float* __restrict__ logits) {
+  constexpr int kTok = 128, kExp = 64, kLd = 72;   // LDS row stride, bf16 elements
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][(kTok + kExp) * kLd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r32 = lane & 31, kh = lane >> 5;
+  const int t0 = blockIdx.x * kTok, e0 = blockIdx.y * kExp;
+  // staging: 192 rows x 8 chunks of 16 B = 1536 chunks, 6 per thread
+  const uint16_t* src[6];
+  int ldo[6];
+#pragma unroll
+  for (int c = 0; c < 6; ++c) {
+    const int idx = tid + 256 * c, row = idx >> 3, cc = idx & 7;
+    src[c] = row < kTok ? x + static_cast<int64_t>(min(t0 + row, T - 1)) * H + cc * 8
+                        : wr + static_cast<int64_t>(e0 + row - kTok) * H + cc * 8;
+    ldo[c] = row * kLd + cc * 8;
+  }
+  f32x16 acc[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
+  const int steps = H / 64;
+  uint4 st[6];
+#pragma unroll
+  for (int c = 0; c < 6; ++c) st[c] = *reinterpret_cast<const uint4*>(src[c]);
+#pragma unroll
+  for (int c = 0; c < 6; ++c) *reinterpret_cast<uint4*>(&lds[0][ldo[c]]) = st[c];
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    const int ko = min(s + 1, steps - 1) * 64;
+#pragma unroll
+    for (int c = 0; c < 6; ++c) st[c] = *reinterpret_cast<const uint4*>(src[c] + ko);
+    const uint16_t* bt = &lds[buf][(32 * wave + r32) * kLd + kh * 32];
+    const uint16_t* at = &lds[buf][(kTok + r32) * kLd + kh * 32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 b = *reinterpret_cast<const uint4*>(bt + 8 * i);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint4 av = *reinterpret_cast<const uint4*>(at + 32 * m * kLd + 8 * i);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                         __builtin_bit_cast(bf16x8, b), acc[m], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 6; ++c) *reinterpret_cast<uint4*>(&lds[buf ^ 1][ldo[c]]) = st[c];
+    __syncthreads();
+  }
+  // lane holds experts e0 + 32m + 8(i/4) + 4kh + (i%4) of token t0 + 32w + r32
+  const int t = t0 + 32 * wave + r32;
+  if (t >= T) return;
+  float* dst = logits + static_cast<int64_t>(t) * E + e0 + 4 * kh;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(dst + 32 * m + 8 * g) =
+          make_float4(acc[m][4 * g], acc[m][4 * g + 1], acc[m][4 * g + 2], acc[m][4 * g + 3]);
+}
+
 // fp32 logits: one thread per (token, expert), plain fp32 FMA over H.
 __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict__ x,
                                                          const float* __restrict__ wr, int T, int E,
@@ -174,7 +245,12 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
-  if (a.bf16) {
+  if (a.bf16 && a.T >= 512 && a.E % 64 == 0) {
+    dim3 grid((a.T + 127) / 128, a.E / 64);
+    hipLaunchKernelGGL(router_logits_bf16_tile, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wr), a.T,
+                       a.E, a.H, a.logits);
+  } else if (a.bf16) {
     dim3 grid((a.E + 15) / 16, (a.T + 15) / 16);
     hipLaunchKernelGGL(router_logits_bf16, grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wr), a.T,

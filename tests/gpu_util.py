@@ -12,7 +12,12 @@ from sparse_moe_transformer_sigmoid_amd import inputs as gen
 
 # max-abs-err / max|ref| bounds of the outputs, by weight dtype
 TOL = {gen.F32: 1e-4, gen.BF16: 1e-2, gen.FP8: 5e-2}
-W_RTOL = 1e-6  # routing weights, relative
+# Routing weights, relative.  The logits are fp32 dot products of length H
+# (7168): with partial sums of size ~0.02*sqrt(k) the accumulated rounding is
+# ~2^-24 * 0.02 * H / sqrt(2) ~ 6e-6 absolute; a weight s/sum(s) inherits
+# (1 - s) times that (up to ~0.5 for bias-favoured low scores) plus a few ulp
+# from the sigmoid and the renormalisation, so 1e-5 bounds it.
+W_RTOL = 1e-5
 
 
 def say(msg):

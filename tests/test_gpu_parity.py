@@ -33,6 +33,9 @@ SMALL = [
     (W["small_bf16"].replace(name="small_bf16_hot", bias="hot"), 300),
     (W["small_bf16"].replace(name="small_bf16_noshared", n_shared_experts=0), 50),
     (W["small_bf16"].replace(name="small_bf16_shared2", n_shared_experts=2), 50),
+    # 64 experts and >= 512 tokens: the LDS-tiled router (128-token tiles, ragged tail)
+    (W["small_bf16"].replace(name="small_bf16_e64", n_routed_experts=64), 600),
+    (W["small_grouped_bf16"].replace(name="small_grouped_bf16_e64", n_routed_experts=64), 520),
     (W["small_fp8"], 1), (W["small_fp8"], 7), (W["small_fp8"], 100), (W["small_fp8"], 300),
     (W["small_fp8"].replace(name="small_fp8_hot", bias="hot"), 200),
     (W["small_fp8"].replace(name="small_fp8_noshared", n_shared_experts=0), 50),
