@@ -249,8 +249,9 @@ namespace moe {
 // rows (decode), the LDS-tiled MFMA kernels (128 rows) beyond that.
 int ffn_tile_rows(const FfnArgs& a, int weight_dtype, int act_dtype) {
   if (act_dtype == MOE_F32) return 16;
-  if (weight_dtype == MOE_FP8_E4M3) return fp8_tile_rows();
   const bool many_rows = static_cast<int64_t>(a.T) * a.k >= 32LL * a.E;
+  if (weight_dtype == MOE_FP8_E4M3)
+    return many_rows && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? tile_fp8_rows() : fp8_tile_rows();
   return many_rows && tile_shapes_ok(a.H, a.F, a.Fs) ? tile_rows() : 16;
 }
 
@@ -258,7 +259,8 @@ hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hip
   if (act_dtype == MOE_F32) return launch_simple_f32(a, true, st);
   if (weight_dtype == MOE_BF16)
     return a.bm == tile_rows() ? launch_gate_up_tile(a, st) : launch_gate_up_stream(a, st);
-  if (weight_dtype == MOE_FP8_E4M3) return launch_gate_up_fp8(a, st);
+  if (weight_dtype == MOE_FP8_E4M3)
+    return a.bm == tile_fp8_rows() ? launch_gate_up_tile_fp8(a, st) : launch_gate_up_fp8(a, st);
   return hipErrorNotSupported;
 }
 
@@ -266,7 +268,8 @@ hipError_t launch_down(const FfnArgs& a, int act_dtype, int weight_dtype, hipStr
   if (act_dtype == MOE_F32) return launch_simple_f32(a, false, st);
   if (weight_dtype == MOE_BF16)
     return a.bm == tile_rows() ? launch_down_tile(a, st) : launch_down_stream(a, st);
-  if (weight_dtype == MOE_FP8_E4M3) return launch_down_fp8(a, st);
+  if (weight_dtype == MOE_FP8_E4M3)
+    return a.bm == tile_fp8_rows() ? launch_down_tile_fp8(a, st) : launch_down_fp8(a, st);
   return hipErrorNotSupported;
 }
 

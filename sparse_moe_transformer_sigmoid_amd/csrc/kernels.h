@@ -109,3 +109,11 @@ struct CombineArgs {
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t st);
 
 }  // namespace moe
+
+namespace moe {
+// ffn_tile_fp8.hip
+hipError_t launch_gate_up_tile_fp8(const FfnArgs& a, hipStream_t st);
+hipError_t launch_down_tile_fp8(const FfnArgs& a, hipStream_t st);
+int tile_fp8_rows();
+bool tile_fp8_shapes_ok(int H, int F, int Fs);
+}  // namespace moe
