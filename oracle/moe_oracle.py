@@ -198,7 +198,10 @@ def route(x, router_w, router_bias, *, num_experts_per_tok: int, n_group: int = 
 
 
 def selection_gap(r: Route, k: int) -> np.ndarray:
-    """Per token: (k-th largest eligible sel) - ((k+1)-th largest eligible sel)."""
+    """Per token: (k-th largest eligible sel) - ((k+1)-th largest eligible sel);
+    infinite when every expert is chosen (no (k+1)-th)."""
+    if k >= r.sel.shape[1]:
+        return np.full(r.sel.shape[0], np.inf)
     masked = np.where(r.eligible, r.sel, -np.inf)
     srt = -np.sort(-masked, axis=1)
     return srt[:, k - 1] - srt[:, k]

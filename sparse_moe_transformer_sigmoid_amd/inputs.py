@@ -115,6 +115,14 @@ WORKLOADS: Dict[str, Workload] = {
     "k2_prefill_bf16_zipf": _k2("k2_prefill_bf16_zipf", 8192, bias="zipf"),
     "k2_fp8": _k2("k2_fp8", 4096, weight_dtype=FP8),
     "dsv3_decode_bf16": _k2("dsv3_decode_bf16", 128, n_routed_experts=256, n_group=8, topk_group=4),
+    # Moonlight-16B MoE shape ("Kimi K2 Base" comparison table): hidden 2048,
+    # 64 routed experts top-6, 2 shared, moe_intermediate 1408
+    "moonlight_bf16": Workload("moonlight_bf16", 256, 2048, 1408, 64, 6, n_shared_experts=2),
+    # the dense first layer (first_k_dense_replace 1, intermediate_size 18432)
+    # as one always-selected expert of weight 1: E = 1, k = 1, no shared
+    "k2_dense_layer_bf16": _k2("k2_dense_layer_bf16", 128, moe_intermediate_size=18432, n_routed_experts=1,
+                               num_experts_per_tok=1, n_shared_experts=0, routed_scaling_factor=1.0,
+                               bias="zero"),
     # small shapes that still span several tiles and a ragged tail
     "small_bf16": Workload("small_bf16", 100, 512, 256, 32, 8),
     "small_fp8": Workload("small_fp8", 100, 512, 256, 32, 8, weight_dtype=FP8),

@@ -204,6 +204,34 @@ def test_k2_fp8_full_size(k2_fp8_weights, T):
         check_sampled(wl, case, out, [0, T - 1] if T > 1 else [0])
 
 
+@pytest.mark.parametrize("T", [64, 256, 7])
+def test_moonlight_shape_full_size(T):
+    """Second MoE shape on the pages (Moonlight-16B: hidden 2048, 64 experts
+    top-6, 2 shared, d_ff 1408), compared element by element."""
+    wl = W["moonlight_bf16"]
+    case = small_case(wl, T)
+    out, ids, w = run_layer(wl, case)
+    ref, route = cases.oracle_forward(wl, case)
+    check_route(ids, w, route)
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL[wl.weight_dtype]
+
+
+@pytest.mark.parametrize("T", [1, 128, 1024])
+def test_dense_first_layer_full_size(T):
+    """The dense first layer (SwiGLU 7168 -> 18432 -> 7168) as E = 1, k = 1,
+    scale 1 through the same entry point; every row compared."""
+    wl = W["k2_dense_layer_bf16"]
+    case = small_case(wl, T)
+    out, ids, w = run_layer(wl, case)
+    assert torch.all(ids == 0) and torch.all(w == 1.0)
+    ref, _ = cases.oracle_forward(wl, case)
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL[wl.weight_dtype]
+
+
 @pytest.mark.parametrize("T", [1, 8, 32, 128, 512])
 def test_dsv3_grouped_decode_full_size(k2_weights, T):
     wl = W["dsv3_decode_bf16"]

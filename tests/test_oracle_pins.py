@@ -73,6 +73,37 @@ def test_p2_ep128_footprints_match_section_2_1():
     check_ep128_footprint()
 
 
+def test_dense_layer_params_match_a_few_hundred_mb():
+    # first_k_dense_replace 1 with intermediate_size 18432 ("Kimi K2 Base" raw
+    # config fields): one SwiGLU of 3 x 7168 x 18432 parameters, which at the
+    # fp8 checkpoint's 1 B/param is "a few hundred MB" ("Behind Kimi-K2's
+    # Config", section 2.3)
+    n = om.expert_params(7168, 18432)
+    assert n == 396_361_728
+    assert 100e6 < n * 1 < 1e9
+    wl = gen.WORKLOADS["k2_dense_layer_bf16"]
+    assert (wl.n_routed_experts, wl.num_experts_per_tok, wl.n_shared_experts) == (1, 1, 0)
+    assert wl.routed_scaling_factor == 1.0
+
+
+def test_dense_layer_as_single_expert_is_plain_swiglu():
+    # E = 1, k = 1, scale 1: the routed layer reduces to the expert itself
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((5, 24))
+    ex, _ = small_weights(11, 1, 24, F=40)
+    out, r = oracle.layer_forward(x, rng.standard_normal((1, 24)), np.zeros(1), lambda e: ex[0], None,
+                                  num_experts_per_tok=1, routed_scaling_factor=1.0)
+    assert np.all(r.weights == 1.0)
+    np.testing.assert_allclose(out, torch_swiglu(x, *ex[0]), rtol=1e-12, atol=1e-12)
+
+
+def test_moonlight_workload_matches_comparison_table():
+    # "Kimi K2 Base" field comparison vs Moonlight 16B
+    wl = gen.WORKLOADS["moonlight_bf16"]
+    assert (wl.hidden_size, wl.n_routed_experts, wl.num_experts_per_tok, wl.n_shared_experts,
+            wl.moe_intermediate_size) == (2048, 64, 6, 2, 1408)
+
+
 def test_p12_prefill_flop_ratio_closed_form():
     # activated flops per token barely change between 256 and 384 experts
     # ("Behind Kimi-K2's Config", section 2.1, Prefill bullet)
