@@ -4,7 +4,10 @@
 One step = one moe_layer_forward (router, grouping, expert FFNs, combine) over
 one batch of synthetic tokens whose inputs are already resident in HBM.
 Default workload: Kimi-K2 decode, T = 128 tokens, bf16, all 384 experts + 1
-shared resident.  Prints ONE JSON line (value = tokens/s) with:
+shared resident.  For an expert-parallel rank workload (ep_size > 1) a step
+is that rank's expert FFN share (moe_expert_ffn over the rows dispatched to
+its local experts plus the shared expert over its own tokens), and value is
+the rank's own tokens per second.  Prints ONE JSON line (value = tokens/s) with:
   roofline      -- the dominant kernel (grouped gate_up GEMM): algorithmic
                    bytes or flops per launch / its mean duration, timed with
                    HIP events the library records around that launch;
@@ -86,13 +89,16 @@ def weight_bytes_per_expert_gate_up(wl: gen.Workload, F: int) -> int:
     return 2 * F * H * (4 if wl.weight_dtype == gen.F32 else 2)
 
 
-def roofline(wl: gen.Workload, T: int, n_active: int, gate_up_ms: float, traffic):
-    """Algorithmic work of one gate_up launch against the bound it sits on."""
+def roofline(wl: gen.Workload, T: int, n_active: int, gate_up_ms: float, traffic, routed_rows=None):
+    """Algorithmic work of one gate_up launch against the bound it sits on:
+    the weights of the active and the shared experts once (bytes), and
+    2 * 2 * rows * H * F for the gate and up products (flops)."""
     F, Fs, H, k = wl.moe_intermediate_size, wl.shared_intermediate_size, wl.hidden_size, wl.num_experts_per_tok
+    rows = T * k if routed_rows is None else routed_rows
     bytes_ = n_active * weight_bytes_per_expert_gate_up(wl, F)
     if Fs:
         bytes_ += weight_bytes_per_expert_gate_up(wl, Fs)
-    flops = 4.0 * (T * k * F + T * Fs) * H
+    flops = 4.0 * (rows * F + T * Fs) * H
     peak_tf = PEAK_TFLOPS[wl.weight_dtype]
     ridge = peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
     sec = gate_up_ms * 1e-3
@@ -169,6 +175,34 @@ def cpu_baseline(wl, case, T, budget_s):
                       f"fp64 numpy, {dt:.1f} s", "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def setup_rank(wl: gen.Workload):
+    """One expert-parallel rank: its own tokens (shared expert) and the rows
+    dispatched to its local experts, grouped by expert, in a buffer of T * cap
+    rows (cap = rows per local token, rounded up)."""
+    counts = gen.gen_dispatch_counts(wl)
+    R, T = int(counts.sum()), wl.num_tokens
+    cap = max(1, -(-R // T))
+    rows = torch.zeros((T * cap, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda")
+    rows[:R] = gen.gen_dispatched_rows(wl, R).cuda()
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    d = {"x": gen.gen_x(wl).cuda(), "x_rows": rows, "offsets": offsets}
+    d.update(gen.gen_expert_weights(wl, device="cuda"))
+    torch.cuda.synchronize()
+    return d, cap, R, int((counts > 0).sum())
+
+
+def make_rank_step(cfg, weights, wl, case, T):
+    """The rank's share between the dispatch and combine exchanges: one
+    moe_expert_ffn over the dispatched rows plus the shared expert."""
+    y = torch.empty_like(case["x_rows"])
+    y_sh = torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda")
+    ws = B.alloc_workspace(cfg, T)
+
+    def step():
+        B.moe_expert_ffn(cfg, weights, case["x"], case["x_rows"], None, case["offsets"], y, y_sh, ws)
+    return step, None
+
+
 def make_step(cfg, weights, wl, case, T):
     """One layer step on pre-allocated buffers (inputs resident in HBM)."""
     out = torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda")
@@ -181,15 +215,15 @@ def make_step(cfg, weights, wl, case, T):
     return step, ids
 
 
-def measure(cfg, weights, wl, case, T, steps, warmup, hip):
+def measure(cfg, weights, wl, case, T, steps, warmup, hip, factory=make_step):
     """Time `steps` layer steps after `warmup` untimed ones (synchronised on
     both sides); the gate_up launch of every timed step is bracketed by HIP
     events the library records on its own stream."""
-    step, ids = make_step(cfg, weights, wl, case, T)
+    step, ids = factory(cfg, weights, wl, case, T)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    n_active = int(torch.unique(ids).numel())
+    n_active = int(torch.unique(ids).numel()) if ids is not None else None
     evs = [(hip.event(), hip.event()) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -259,11 +293,24 @@ def main():
     wl = gen.WORKLOADS[args.workload]
     T = args.tokens or wl.num_tokens
     B.load()
-    case = setup(wl, T)
     hip = Hip()
-    cfg = B.MoeConfig.from_fields(wl.fields())
+    rank = wl.ep_size > 1
+    routed_rows = None
+    if rank:
+        if args.tokens or args.sweep_tokens or not args.no_cpu_baseline:
+            print("an expert-parallel rank workload runs at its own token count, without the oracle "
+                  "baseline (pass --no-cpu-baseline)", file=sys.stderr)
+            sys.exit(2)
+        case, cap, routed_rows, n_local = setup_rank(wl)
+        cfg = B.MoeConfig.from_fields(dict(wl.fields(), num_experts_per_tok=cap))
+    else:
+        case = setup(wl, T)
+        cfg = B.MoeConfig.from_fields(wl.fields())
     weights = B.MoeWeights.from_tensors(case)
-    step, wall, gate_up_ms, n_active = measure(cfg, weights, wl, case, T, args.steps, args.warmup, hip)
+    step, wall, gate_up_ms, n_active = measure(cfg, weights, wl, case, T, args.steps, args.warmup, hip,
+                                               make_rank_step if rank else make_step)
+    if rank:
+        n_active = n_local
     ms_per_step = wall * 1e3 / args.steps
 
     detail = {}
@@ -292,7 +339,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    rl = roofline(wl, T, n_active, gate_up_ms, stored_traffic(args.workload))
+    rl = roofline(wl, T, n_active, gate_up_ms, stored_traffic(args.workload), routed_rows)
     res = {
         "metric": METRIC, "value": round(T * args.steps / wall, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -305,6 +352,10 @@ def main():
                    "parallelism": "none (one GPU, all experts resident)"},
         "roofline": rl,
     }
+    if rank:
+        res["config"].update(parallelism=f"one rank of ep{wl.ep_size} (its expert FFN share only)",
+                             global_experts=wl.n_routed_experts * wl.ep_size, dispatched_rows=routed_rows,
+                             row_capacity_per_token=cap)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, case, T, args.cpu_budget)
     recs = sweep(args, wl, case, cfg, weights, hip) if args.sweep_tokens else []

@@ -57,7 +57,7 @@ typedef struct {
   int32_t hidden_size;           /* H; multiple of 128                          */
   int32_t moe_intermediate_size; /* F; multiple of 128                          */
   int32_t n_routed_experts;      /* E; 1..1023                                  */
-  int32_t num_experts_per_tok;   /* k; 1..min(E, 32)                            */
+  int32_t num_experts_per_tok;   /* k; 1..32, and <= E where routing reads it    */
   int32_t n_shared_experts;      /* 0..8; shared width Fs = n_shared * F         */
   int32_t n_group;               /* >= 1, divides E, <= 64                       */
   int32_t topk_group;            /* 1..n_group; k <= topk_group * E / n_group    */
@@ -125,7 +125,18 @@ moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* 
  * and 128 channels before the down projection; weights are code * block scale.
  * x [T][H] act_dtype; x_perm/x_perm_scales as produced by moe_permute;
  * expert_offsets [E+1]; y_perm [T*k][H] act_dtype; y_shared [T][H] act_dtype
- * (ignored when n_shared_experts == 0). */
+ * (ignored when n_shared_experts == 0).
+ * Only the rows [0, offsets[E]) of x_perm / y_perm are used; rows after it
+ * are left untouched.  Each segment is clamped into [0, T*k] on the device,
+ * so no offsets array makes the kernels leave the buffers.
+ * Expert parallelism ("Behind Kimi-K2's Config" section 2.1: at EP=128 a
+ * DeepSeek-V3 rank holds 2 routed + 1 shared expert per layer, so K2's 384
+ * give 3 + 1): one rank's share is
+ * this call with E = its local expert count, x_perm = the rows dispatched to
+ * it grouped by local expert, x / T = its own tokens for the shared expert,
+ * and k any row capacity per token with T*k >= offsets[E].  This entry point
+ * therefore does not apply the routing constraints (k <= E, n_group,
+ * topk_group); k is 1..32. */
 moe_status_t moe_expert_ffn(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
                             const void* x_perm, const float* x_perm_scales,
                             const int32_t* expert_offsets, int64_t num_tokens, void* y_perm,

@@ -62,7 +62,10 @@ int act_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
 bool fp8(const moe_config_t* c) { return c->weight_dtype == MOE_FP8_E4M3; }
 int shared_F(const moe_config_t* c) { return c->n_shared_experts * c->moe_intermediate_size; }
 
-moe_status_t check_cfg(const moe_config_t* c) {
+// `routing`: also check the fields only routing reads (k <= E, groups).  The
+// expert FFN alone takes k as a row capacity per token, so one expert-parallel
+// rank can hold fewer local experts than a token selects.
+moe_status_t check_cfg(const moe_config_t* c, bool routing = true) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
   if (c->scoring_func != MOE_SCORING_SIGMOID)
     return fail(MOE_ERR_UNSUPPORTED, "scoring_func %d: only sigmoid (0) is implemented", c->scoring_func);
@@ -73,15 +76,18 @@ moe_status_t check_cfg(const moe_config_t* c) {
   if (H <= 0 || H % 128 || F <= 0 || F % 128)
     return fail(MOE_ERR_INVALID_ARG, "hidden_size %d and moe_intermediate_size %d must be positive multiples of 128", H, F);
   if (E < 1 || E > 1023) return fail(MOE_ERR_INVALID_ARG, "n_routed_experts %d not in 1..1023", E);
-  if (k < 1 || k > std::min(E, 32)) return fail(MOE_ERR_INVALID_ARG, "num_experts_per_tok %d not in 1..min(E, 32)", k);
+  if (k < 1 || k > 32) return fail(MOE_ERR_INVALID_ARG, "num_experts_per_tok %d not in 1..32", k);
   if (c->n_shared_experts < 0 || c->n_shared_experts > 8)
     return fail(MOE_ERR_INVALID_ARG, "n_shared_experts %d not in 0..8", c->n_shared_experts);
-  if (c->n_group < 1 || c->n_group > 64 || E % c->n_group)
-    return fail(MOE_ERR_INVALID_ARG, "n_group %d must divide n_routed_experts %d and be <= 64", c->n_group, E);
-  if (c->topk_group < 1 || c->topk_group > c->n_group)
-    return fail(MOE_ERR_INVALID_ARG, "topk_group %d not in 1..n_group", c->topk_group);
-  if (k > c->topk_group * (E / c->n_group))
-    return fail(MOE_ERR_INVALID_ARG, "num_experts_per_tok %d exceeds the experts of topk_group groups", k);
+  if (routing) {
+    if (k > E) return fail(MOE_ERR_INVALID_ARG, "num_experts_per_tok %d exceeds n_routed_experts %d", k, E);
+    if (c->n_group < 1 || c->n_group > 64 || E % c->n_group)
+      return fail(MOE_ERR_INVALID_ARG, "n_group %d must divide n_routed_experts %d and be <= 64", c->n_group, E);
+    if (c->topk_group < 1 || c->topk_group > c->n_group)
+      return fail(MOE_ERR_INVALID_ARG, "topk_group %d not in 1..n_group", c->topk_group);
+    if (k > c->topk_group * (E / c->n_group))
+      return fail(MOE_ERR_INVALID_ARG, "num_experts_per_tok %d exceeds the experts of topk_group groups", k);
+  }
   const bool ok_dt = (c->act_dtype == MOE_F32 && c->weight_dtype == MOE_F32) ||
                      (c->act_dtype == MOE_BF16 && c->weight_dtype == MOE_BF16) ||
                      (c->act_dtype == MOE_BF16 && c->weight_dtype == MOE_FP8_E4M3);
@@ -249,8 +255,10 @@ moe_status_t run_permute(const moe_config_t* c, const int32_t* ids, int64_t T, i
 moe_status_t run_ffn(const moe_config_t* c, const moe_weights_t* w, FfnArgs& f, int64_t T,
                      void* ws, hipStream_t st) {
   const Layout L = layout(c, T);
-  const int bm = ffn_tile_rows(f, c->weight_dtype, c->act_dtype);
+  const FfnPlan plan = ffn_plan(f, c->weight_dtype, c->act_dtype);
+  const int bm = plan.bm;
   f.bm = bm;
+  f.kind = plan.kind;
   f.tiles = at<Tile>(ws, L.tiles);
   f.tile_count = at<int32_t>(ws, L.tcount);
   f.tile_bound = max_tiles(T, f.k, f.E, f.Fs > 0, bm);
@@ -274,6 +282,7 @@ moe_status_t run_ffn(const moe_config_t* c, const moe_weights_t* w, FfnArgs& f, 
   ta.E = f.E;
   ta.bm = bm;
   ta.shared = f.Fs > 0;
+  ta.cap = f.tile_bound;
   ta.tiles = const_cast<Tile*>(f.tiles);
   ta.tile_count = const_cast<int32_t*>(f.tile_count);
   MOE_LAUNCH(MOE_KID_TILES, launch_build_tiles(ta, st));
@@ -321,7 +330,7 @@ const char* moe_status_string(moe_status_t s) {
 const char* moe_last_error(void) { return g_err.c_str(); }
 
 size_t moe_workspace_size(const moe_config_t* cfg, int64_t T) {
-  if (check_cfg(cfg) != MOE_OK || T < 0) return 0;
+  if (check_cfg(cfg, false) != MOE_OK || T < 0) return 0;
   return layout(cfg, T).total;
 }
 
@@ -391,7 +400,7 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, const moe_weights_t* w, con
                             const int32_t* expert_offsets, int64_t T, void* y_perm, void* y_shared,
                             void* ws, size_t ws_bytes, void* stream) {
   g_err.clear();
-  TRY(check_cfg(cfg));
+  TRY(check_cfg(cfg, false));
   TRY(check_T(T));
   if (T == 0) return MOE_OK;
   TRY(check_weights(cfg, w));

@@ -22,65 +22,88 @@ namespace {
 
 constexpr int kWK = 4;  // waves splitting K
 
-template <int NA>
+// K elements per wave step: 128 for up to 32 rows, then halved as the row
+// sub-tiles grow so that the double-buffered fragments stay in registers
+template <int NT>
+constexpr int step_k() { return NT <= 2 ? 128 : (NT == 4 ? 64 : 32); }
+
+// One wave's operands for one K step: NA weight row-tiles and NT token
+// sub-tiles of 16 rows, KS / 32 uint4 (8 bf16) per lane and row.
+template <int NA, int NT, int KS>
 struct Frag {
-  uint4 a[NA][4];
-  uint4 b[4];
+  uint4 a[NA][KS / 32];
+  uint4 b[NT][KS / 32];
 };
 
-template <int NA>
-__device__ __forceinline__ void load_frag(Frag<NA>& f, const uint16_t* const (&pa)[NA],
-                                          const uint16_t* pb, int koff) {
+template <int NA, int NT, int KS>
+__device__ __forceinline__ void load_frag(Frag<NA, NT, KS>& f, const uint16_t* const (&pa)[NA],
+                                          const uint16_t* const (&pb)[NT], int koff) {
 #pragma unroll
   for (int m = 0; m < NA; ++m) {
     const uint4* s = reinterpret_cast<const uint4*>(pa[m] + koff);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[m][i] = s[i];
+    for (int i = 0; i < KS / 32; ++i) f.a[m][i] = s[i];
   }
-  const uint4* s = reinterpret_cast<const uint4*>(pb + koff);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.b[i] = s[i];
+  for (int n = 0; n < NT; ++n) {
+    const uint4* s = reinterpret_cast<const uint4*>(pb[n] + koff);
+#pragma unroll
+    for (int i = 0; i < KS / 32; ++i) f.b[n][i] = s[i];
+  }
 }
 
-template <int NA>
-__device__ __forceinline__ void mma_frag(const Frag<NA>& f, f32x4 (&acc)[NA]) {
+template <int NA, int NT, int KS>
+__device__ __forceinline__ void mma_frag(const Frag<NA, NT, KS>& f, f32x4 (&acc)[NA][NT]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < KS / 32; ++i)
 #pragma unroll
-    for (int m = 0; m < NA; ++m)
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.a[m][i]),
-                                                       __builtin_bit_cast(bf16x8, f.b[i]), acc[m],
-                                                       0, 0, 0);
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int m = 0; m < NA; ++m)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.a[m][i]),
+                                                            __builtin_bit_cast(bf16x8, f.b[n][i]),
+                                                            acc[m][n], 0, 0, 0);
 }
 
 // K loop of one wave over steps wave, wave+kWK, ... (double-buffered loads),
-// then the kWK partial sums are added in LDS; wave 0 returns the total.
-template <int NA>
-__device__ __forceinline__ void stream_k(const uint16_t* const (&pa)[NA], const uint16_t* pb,
-                                         int steps, f32x4 (&acc)[NA]) {
-  __shared__ f32x4 red[kWK - 1][NA][64];
+// then the kWK partial sums are added in LDS in wave order; wave 0 returns
+// the total.  Lane (r = lane % 16, q = lane / 16) reads KS/4 contiguous
+// elements at offset q*KS/4 of its row in every step: both operands use the
+// same K order, so the MFMA sums run over the full step.
+template <int NA, int NT, int KS>
+__device__ __forceinline__ void stream_k(const uint16_t* const (&pa)[NA],
+                                         const uint16_t* const (&pb)[NT], int steps,
+                                         f32x4 (&acc)[NA][NT]) {
+  __shared__ f32x4 red[kWK - 1][NA][NT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int m = 0; m < NA; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < NA; ++m)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   int s = wave;
-  Frag<NA> cur, nxt;
-  if (s < steps) load_frag<NA>(cur, pa, pb, s * 128);
+  Frag<NA, NT, KS> cur, nxt;
+  if (s < steps) load_frag(cur, pa, pb, s * KS);
+#pragma unroll 1
   while (s < steps) {
     const int sn = s + kWK;
-    if (sn < steps) load_frag<NA>(nxt, pa, pb, sn * 128);
-    mma_frag<NA>(cur, acc);
+    if (sn < steps) load_frag(nxt, pa, pb, sn * KS);
+    mma_frag(cur, acc);
     cur = nxt;
     s = sn;
   }
   if (wave > 0)
 #pragma unroll
-    for (int m = 0; m < NA; ++m) red[wave - 1][m][lane] = acc[m];
+    for (int m = 0; m < NA; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) red[wave - 1][m][n][lane] = acc[m][n];
   __syncthreads();
   if (wave == 0)
-#pragma unroll
+#pragma unroll 1
     for (int w = 0; w < kWK - 1; ++w)
 #pragma unroll
-      for (int m = 0; m < NA; ++m) acc[m] += red[w][m][lane];
+      for (int m = 0; m < NA; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[m][n] += red[w][m][n][lane];
 }
 
 __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
@@ -92,8 +115,13 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, fl
 
 }  // namespace
 
-// gate_up: block = 16 intermediate features of one tile
+// gate_up: block = 16 intermediate features (16 gate + 16 up weight rows) of
+// one work item of up to 16*NT grouped rows.  Sub-tiles past the item's rows
+// read its last row again (in bounds, not stored), which keeps the K loop
+// free of divergent control flow.
+template <int NT>
 __global__ __launch_bounds__(256) void gate_up_stream_bf16(FfnArgs a) {
+  constexpr int KS = step_k<NT>();
   const int ti = blockIdx.y;
   if (ti >= *a.tile_count) return;
   const Tile tl = a.tiles[ti];
@@ -106,49 +134,65 @@ __global__ __launch_bounds__(256) void gate_up_stream_bf16(FfnArgs a) {
   const uint16_t* wg = static_cast<const uint16_t*>(sh ? a.sh_gate : a.w_gate);
   const uint16_t* wu = static_cast<const uint16_t*>(sh ? a.sh_up : a.w_up);
   const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.F * H;
-  const uint16_t* pa[2] = {wg + wofs + (f0 + r) * H + q * 32, wu + wofs + (f0 + r) * H + q * 32};
-  const int64_t p = tl.row0 + min(r, tl.rows - 1);
-  const uint16_t* pb;
-  if (sh) pb = static_cast<const uint16_t*>(a.xs) + (p - TK) * H;
-  else pb = static_cast<const uint16_t*>(a.xr) + (a.xr_rows ? a.xr_rows[p] : p) * H;
-  pb += q * 32;
-  f32x4 acc[2];
-  stream_k<2>(pa, pb, a.H / 128, acc);
-  if ((threadIdx.x >> 6) == 0 && r < tl.rows) {
-    const int64_t pr = tl.row0 + r;
+  const uint16_t* pa[2] = {wg + wofs + (f0 + r) * H + q * (KS / 4), wu + wofs + (f0 + r) * H + q * (KS / 4)};
+  const uint16_t* pb[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int64_t p = tl.row0 + min(16 * n + r, tl.rows - 1);
+    const uint16_t* b = sh ? static_cast<const uint16_t*>(a.xs) + (p - TK) * H
+                           : static_cast<const uint16_t*>(a.xr) + (a.xr_rows ? a.xr_rows[p] : p) * H;
+    pb[n] = b + q * (KS / 4);
+  }
+  f32x4 acc[2][NT];
+  stream_k<2, NT, KS>(pa, pb, a.H / KS, acc);
+  if ((threadIdx.x >> 6) != 0) return;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    if (16 * n + r >= tl.rows) continue;
+    const int64_t pr = tl.row0 + 16 * n + r;
     uint16_t* dst = sh ? static_cast<uint16_t*>(a.h_sh) + (pr - TK) * a.Fs
                        : static_cast<uint16_t*>(a.h) + pr * a.F;
-    store_bf16x4(dst + f0 + 4 * q, silu(acc[0][0]) * acc[1][0], silu(acc[0][1]) * acc[1][1],
-                 silu(acc[0][2]) * acc[1][2], silu(acc[0][3]) * acc[1][3]);
+    store_bf16x4(dst + f0 + 4 * q, silu(acc[0][n][0]) * acc[1][n][0], silu(acc[0][n][1]) * acc[1][n][1],
+                 silu(acc[0][n][2]) * acc[1][n][2], silu(acc[0][n][3]) * acc[1][n][3]);
   }
 }
 
-// down: block = 32 hidden outputs of one tile
+// down: block = 16 * NA hidden outputs of one work item
+template <int NT, int NA>
 __global__ __launch_bounds__(256) void down_stream_bf16(FfnArgs a) {
+  constexpr int KS = step_k<NT>();
   const int ti = blockIdx.y;
   if (ti >= *a.tile_count) return;
   const Tile tl = a.tiles[ti];
   const bool sh = tl.group == a.E;
   const int Fg = sh ? a.Fs : a.F;
-  const int h0 = blockIdx.x * 32;
+  const int h0 = blockIdx.x * 16 * NA;
   const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
   const int64_t TK = static_cast<int64_t>(a.T) * a.k;
   const uint16_t* wd = static_cast<const uint16_t*>(sh ? a.sh_down : a.w_down);
   const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.H * a.F;
-  const uint16_t* pa[2] = {wd + wofs + static_cast<int64_t>(h0 + r) * Fg + q * 32,
-                           wd + wofs + static_cast<int64_t>(h0 + 16 + r) * Fg + q * 32};
-  const int64_t p = tl.row0 + min(r, tl.rows - 1);
-  const uint16_t* pb = sh ? static_cast<const uint16_t*>(a.h_sh) + (p - TK) * a.Fs
-                          : static_cast<const uint16_t*>(a.h) + p * a.F;
-  pb += q * 32;
-  f32x4 acc[2];
-  stream_k<2>(pa, pb, Fg / 128, acc);
-  if ((threadIdx.x >> 6) == 0 && r < tl.rows) {
-    const int64_t pr = tl.row0 + r;
+  const uint16_t* pa[NA];
+#pragma unroll
+  for (int m = 0; m < NA; ++m) pa[m] = wd + wofs + static_cast<int64_t>(h0 + 16 * m + r) * Fg + q * (KS / 4);
+  const uint16_t* pb[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int64_t p = tl.row0 + min(16 * n + r, tl.rows - 1);
+    pb[n] = (sh ? static_cast<const uint16_t*>(a.h_sh) + (p - TK) * a.Fs
+                : static_cast<const uint16_t*>(a.h) + p * a.F) + q * (KS / 4);
+  }
+  f32x4 acc[NA][NT];
+  stream_k<NA, NT, KS>(pa, pb, Fg / KS, acc);
+  if ((threadIdx.x >> 6) != 0) return;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    if (16 * n + r >= tl.rows) continue;
+    const int64_t pr = tl.row0 + 16 * n + r;
     uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (pr - TK) * a.H
                        : static_cast<uint16_t*>(a.y) + pr * a.H;
-    store_bf16x4(dst + h0 + 4 * q, acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
-    store_bf16x4(dst + h0 + 16 + 4 * q, acc[1][0], acc[1][1], acc[1][2], acc[1][3]);
+#pragma unroll
+    for (int m = 0; m < NA; ++m)
+      store_bf16x4(dst + h0 + 16 * m + 4 * q, acc[m][n][0], acc[m][n][1], acc[m][n][2], acc[m][n][3]);
   }
 }
 
@@ -215,15 +259,27 @@ __global__ __launch_bounds__(256) void down_simple_f32(FfnArgs a) {
   dst[o] = y;
 }
 
+// sub-tiles of 16 rows per work item: bm = 16 * NT
 hipError_t launch_gate_up_stream(const FfnArgs& a, hipStream_t st) {
-  dim3 grid(std::max(a.F, a.Fs) / 16, static_cast<unsigned>(a.tile_bound));
-  hipLaunchKernelGGL(gate_up_stream_bf16, grid, dim3(256), 0, st, a);
+  const dim3 grid(std::max(a.F, a.Fs) / 16, static_cast<unsigned>(a.tile_bound));
+  switch (a.bm) {
+    case 16: hipLaunchKernelGGL(gate_up_stream_bf16<1>, grid, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(gate_up_stream_bf16<2>, grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(gate_up_stream_bf16<4>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
+// 32 outputs per block
 hipError_t launch_down_stream(const FfnArgs& a, hipStream_t st) {
-  dim3 grid(a.H / 32, static_cast<unsigned>(a.tile_bound));
-  hipLaunchKernelGGL(down_stream_bf16, grid, dim3(256), 0, st, a);
+  const unsigned tiles = static_cast<unsigned>(a.tile_bound);
+  switch (a.bm) {
+    case 16: hipLaunchKernelGGL((down_stream_bf16<1, 2>), dim3(a.H / 32, tiles), dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((down_stream_bf16<2, 2>), dim3(a.H / 32, tiles), dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((down_stream_bf16<4, 2>), dim3(a.H / 32, tiles), dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -243,33 +299,47 @@ hipError_t launch_simple_f32(const FfnArgs& a, bool gate_up, hipStream_t st) {
 
 namespace moe {
 
-// rows per work-list tile for the kernel a call will use
-// Rows per work-list tile, which also selects the kernel family: the
-// weight-streaming kernels (16 rows) while experts average fewer than 32
-// rows (decode), the LDS-tiled MFMA kernels (128 rows) beyond that.
-int ffn_tile_rows(const FfnArgs& a, int weight_dtype, int act_dtype) {
-  if (act_dtype == MOE_F32) return 16;
-  const bool many_rows = static_cast<int64_t>(a.T) * a.k >= 32LL * a.E;
+// Rows per work-list tile and the kernel family of one call, from the
+// expected rows per expert (T*k / E; the row capacity for one rank's share).
+// Measured on MI355X over Kimi-K2 decode (T = 128..1024), the DeepSeek-V3
+// and Moonlight shapes, expert-parallel rank shares and the dense layer:
+//  * LDS-tiled MFMA kernels (128 rows x 512 or 256 weight rows per block) from
+//    32 rows per expert on, while the down projection's tiled grid still has
+//    64 blocks or more (a single 7168-wide dense layer at 128 tokens has 14);
+//  * else the weight-streaming kernels with work items of 16 rows below 6
+//    rows per expert, 32 below 12 and 64 beyond (an expert of up to 64 rows
+//    then streams its weights once; 128-row items run at half occupancy and
+//    were slower in every case).
+FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
+  if (act_dtype == MOE_F32) return {16, FfnPlan::kSimple};
+  const int64_t rows = static_cast<int64_t>(a.T) * a.k;
+  const double per_expert = static_cast<double>(rows) / a.E;
+  const bool many_rows = per_expert >= 32.0;
   if (weight_dtype == MOE_FP8_E4M3)
-    return many_rows && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? tile_fp8_rows() : fp8_tile_rows();
-  return many_rows && tile_shapes_ok(a.H, a.F, a.Fs) ? tile_rows() : 16;
+    return many_rows && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? FfnPlan{tile_fp8_rows(), FfnPlan::kTiled}
+                                                           : FfnPlan{fp8_tile_rows(), FfnPlan::kStream};
+  const int64_t tiled_items = (rows + 127) / 128 + (a.Fs > 0 ? (a.T + 127) / 128 : 0);
+  if (many_rows && tile_shapes_ok(a.H, a.F, a.Fs) && tiled_items * (a.H / 512) >= 64)
+    return {tile_rows(), FfnPlan::kTiled};
+  const int bm = per_expert < 6.0 ? 16 : (per_expert < 12.0 ? 32 : 64);
+  return {bm, FfnPlan::kStream};
 }
 
 hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {
   if (act_dtype == MOE_F32) return launch_simple_f32(a, true, st);
   if (weight_dtype == MOE_BF16)
-    return a.bm == tile_rows() ? launch_gate_up_tile(a, st) : launch_gate_up_stream(a, st);
+    return a.kind == FfnPlan::kTiled ? launch_gate_up_tile(a, st) : launch_gate_up_stream(a, st);
   if (weight_dtype == MOE_FP8_E4M3)
-    return a.bm == tile_fp8_rows() ? launch_gate_up_tile_fp8(a, st) : launch_gate_up_fp8(a, st);
+    return a.kind == FfnPlan::kTiled ? launch_gate_up_tile_fp8(a, st) : launch_gate_up_fp8(a, st);
   return hipErrorNotSupported;
 }
 
 hipError_t launch_down(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {
   if (act_dtype == MOE_F32) return launch_simple_f32(a, false, st);
   if (weight_dtype == MOE_BF16)
-    return a.bm == tile_rows() ? launch_down_tile(a, st) : launch_down_stream(a, st);
+    return a.kind == FfnPlan::kTiled ? launch_down_tile(a, st) : launch_down_stream(a, st);
   if (weight_dtype == MOE_FP8_E4M3)
-    return a.bm == tile_fp8_rows() ? launch_down_tile_fp8(a, st) : launch_down_fp8(a, st);
+    return a.kind == FfnPlan::kTiled ? launch_down_tile_fp8(a, st) : launch_down_fp8(a, st);
   return hipErrorNotSupported;
 }
 

@@ -36,6 +36,7 @@ struct TileArgs {
   const int32_t* offsets;  // [E+1]
   int T, k, E, bm;
   bool shared;             // append the shared group (rows T*k + t)
+  int64_t cap;             // capacity of `tiles`
   Tile* tiles;
   int32_t* tile_count;
 };
@@ -60,6 +61,7 @@ struct FfnArgs {
   const int32_t* tile_count;
   int64_t tile_bound;  // grid size along tiles
   int bm;              // rows per tile used to build `tiles`
+  int kind;            // FfnPlan::Kind of the kernels to launch
   const int32_t* offsets;  // [E+1] (simple fp32 kernels)
   // weights (dtype per mode); routed [E][F][H] / [E][H][F], shared [Fs][H] / [H][Fs]
   const void *w_gate, *w_up, *w_down, *sh_gate, *sh_up, *sh_down;
@@ -85,7 +87,12 @@ struct FfnArgs {
 };
 hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st);
 hipError_t launch_down(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st);
-int ffn_tile_rows(const FfnArgs& a, int weight_dtype, int act_dtype);
+struct FfnPlan {
+  enum Kind { kSimple = 0, kStream = 1, kTiled = 2 };
+  int bm;    // rows per work-list tile
+  int kind;
+};
+FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype);
 bool tile_shapes_ok(int H, int F, int Fs);
 // per-kernel-family launchers (ffn_stream.hip, ffn_fp8.hip)
 hipError_t launch_gate_up_stream(const FfnArgs& a, hipStream_t st);

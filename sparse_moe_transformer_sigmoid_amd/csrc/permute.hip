@@ -131,23 +131,29 @@ int64_t max_tiles(int64_t T, int k, int E, bool shared, int bm) {
   return rows / bm + std::min<int64_t>(E, rows) + (shared ? (T + bm - 1) / bm : 0);
 }
 
+// Work list of the grouped GEMMs: group g < E covers the rows of expert g,
+// group E the shared expert's T rows after the T*k routed ones.  Offsets come
+// from the caller of moe_expert_ffn, so each segment is clamped into
+// [0, T*k] and at most `cap` tiles are written: any offsets array yields
+// tiles inside the row buffers.
 __global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ offsets, int T,
-                                                    int k, int E, int bm, int shared,
+                                                    int k, int E, int bm, int shared, int cap,
                                                     Tile* __restrict__ tiles,
                                                     int32_t* __restrict__ tile_count) {
   const int g = threadIdx.x;  // groups 0..E (E <= 1023)
+  const int TK = T * k;
   int n = 0, base = 0;
   if (g < E) {
-    base = offsets[g];
-    n = offsets[g + 1] - base;
+    base = min(max(offsets[g], 0), TK);
+    n = min(max(offsets[g + 1], base), TK) - base;
   } else if (g == E && shared) {
-    base = T * k;
+    base = TK;
     n = T;
   }
   const int nt = (n + bm - 1) / bm;
   int all;
   const int start = block_exclusive_scan(nt, &all);
-  for (int i = 0; i < nt; ++i) {
+  for (int i = 0; i < nt && start + i < cap; ++i) {
     Tile t;
     t.group = g;
     t.row0 = base + i * bm;
@@ -155,12 +161,12 @@ __global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ 
     t.pad = 0;
     tiles[start + i] = t;
   }
-  if (g == 0) *tile_count = all;
+  if (g == 0) *tile_count = min(all, cap);
 }
 
 hipError_t launch_build_tiles(const TileArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(build_tiles, dim3(1), dim3(1024), 0, st, a.offsets, a.T, a.k, a.E, a.bm,
-                     a.shared ? 1 : 0, a.tiles, a.tile_count);
+                     a.shared ? 1 : 0, static_cast<int>(a.cap), a.tiles, a.tile_count);
   return hipGetLastError();
 }
 

@@ -46,6 +46,8 @@ TID_SH_UP = 9
 TID_SH_DOWN = 10
 TID_FP8_U = 11
 TID_ZIPF_RANK = 12
+TID_DISPATCH_COUNT = 13
+TID_DISPATCH_ROWS = 14
 
 F32, BF16, FP8 = "f32", "bf16", "fp8_e4m3"
 
@@ -76,6 +78,11 @@ class Workload:
     zipf_beta: float = 0.1
     zipf_s: float = 1.1
     seed: int = 0
+    # > 1: the workload is one expert-parallel rank's share of a model with
+    # n_routed_experts * ep_size experts; num_tokens is the rank's own batch
+    # (which its shared expert serves) and the routed rows arrive dispatched
+    # from a global batch of num_tokens * ep_size tokens
+    ep_size: int = 1
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -123,6 +130,11 @@ WORKLOADS: Dict[str, Workload] = {
     "k2_dense_layer_bf16": _k2("k2_dense_layer_bf16", 128, moe_intermediate_size=18432, n_routed_experts=1,
                                num_experts_per_tok=1, n_shared_experts=0, routed_scaling_factor=1.0,
                                bias="zero"),
+    # one expert-parallel rank's share of the Kimi-K2 layer at decode: 384
+    # experts over 128 ranks (3 routed + the shared expert per rank) or over
+    # 8 ranks (48 routed + shared), 128 tokens per rank
+    "k2_ep128_rank_bf16": _k2("k2_ep128_rank_bf16", 128, n_routed_experts=3, ep_size=128),
+    "k2_ep8_rank_bf16": _k2("k2_ep8_rank_bf16", 128, n_routed_experts=48, ep_size=8),
     # small shapes that still span several tiles and a ragged tail
     "small_bf16": Workload("small_bf16", 100, 512, 256, 32, 8),
     "small_fp8": Workload("small_fp8", 100, 512, 256, 32, 8, weight_dtype=FP8),
@@ -258,6 +270,24 @@ def gen_expert_weights(wl: Workload, device="cpu", experts: Optional[range] = No
             if s is not None:
                 out["sh_s_" + name] = s
     return out
+
+
+def gen_dispatch_counts(wl: Workload, num_tokens: Optional[int] = None) -> np.ndarray:
+    """Rows each local expert of an expert-parallel rank receives: every token
+    of the global batch (num_tokens * ep_size) picks num_experts_per_tok of
+    the n_routed_experts * ep_size experts, so a given expert's count is
+    Binomial(global tokens, k / global experts), drawn independently here."""
+    T = wl.num_tokens if num_tokens is None else num_tokens
+    n_global = T * wl.ep_size
+    p = wl.num_experts_per_tok / (wl.n_routed_experts * wl.ep_size)
+    return _rng(wl.seed, TID_DISPATCH_COUNT, T).binomial(n_global, p, wl.n_routed_experts).astype(np.int64)
+
+
+def gen_dispatched_rows(wl: Workload, n_rows: int) -> torch.Tensor:
+    """Token rows as they arrive from the dispatch exchange (grouped by local
+    expert; each one is some token's layer input, so the same N(0, 1) law)."""
+    a = _rng(wl.seed, TID_DISPATCH_ROWS, n_rows).standard_normal((n_rows, wl.hidden_size), np.float32)
+    return round_to(a, wl.act_dtype)
 
 
 def gen_inputs(wl: Workload, device="cpu", num_tokens: Optional[int] = None) -> Dict[str, torch.Tensor]:

@@ -86,3 +86,36 @@ def oracle_forward(wl: gen.Workload, case: dict, tokens=None):
         to64(case["x"]), to64(case["router_w"]), to64(case["router_bias"]),
         expert_fn(wl, case), shared_weights(wl, case), fp8_act=(wl.weight_dtype == gen.FP8),
         tokens=tokens, **route_kwargs(wl))
+
+
+def make_rank_case(wl: gen.Workload, device="cuda"):
+    """Inputs of one expert-parallel rank (wl.ep_size > 1): its own tokens x
+    (served by the shared expert) and the rows dispatched to its local experts,
+    grouped by expert in a buffer of T * cap rows; cap = rows per local token,
+    rounded up.  Returns (case, cap)."""
+    counts = gen.gen_dispatch_counts(wl)
+    R, T = int(counts.sum()), wl.num_tokens
+    cap = max(1, -(-R // T))
+    rows = torch.zeros((T * cap, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype))
+    rows[:R] = gen.gen_dispatched_rows(wl, R)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    d = {"x": gen.gen_x(wl).to(device), "x_rows": rows.to(device),
+         "offsets": torch.from_numpy(offsets).to(device)}
+    d.update(gen.gen_expert_weights(wl, device))
+    return d, cap
+
+
+def oracle_rank_share(wl: gen.Workload, case: dict):
+    """fp64 oracle of one rank's share: every dispatched row through its local
+    expert's SwiGLU, and the shared expert over the rank's own tokens."""
+    offsets = case["offsets"].cpu().numpy()
+    rows = to64(case["x_rows"])
+    fn = expert_fn(wl, case)
+    y = np.zeros((int(offsets[-1]), wl.hidden_size))
+    for e in range(wl.n_routed_experts):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            y[a:b] = oracle.swiglu_expert(rows[a:b], *fn(e))
+    sh = shared_weights(wl, case)
+    y_sh = oracle.swiglu_expert(to64(case["x"]), *sh) if sh is not None else None
+    return y, y_sh

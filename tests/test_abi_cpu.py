@@ -146,3 +146,30 @@ def test_config_struct_layout_matches_header():
     # 13 int/float fields + int[2], no padding
     assert ctypes.sizeof(B.MoeConfig) == 15 * 4
     assert ctypes.sizeof(B.MoeWeights) == 12 * 8
+
+
+def test_expert_ffn_takes_k_as_row_capacity():
+    """One expert-parallel rank: 3 local experts and a row capacity of 9 per
+    token.  The router rejects k > E; the expert FFN and the workspace size
+    accept it (the FFN then fails later, on its fake weights)."""
+    c = B.MoeConfig.from_fields(dict(gen.WORKLOADS["k2_ep128_rank_bf16"].fields(), num_experts_per_tok=9))
+    assert route(c) == B.MOE_ERR_INVALID_ARG and "exceeds n_routed_experts" in B.moe_last_error()
+    assert B.moe_workspace_size(c, 128) > 0
+    lib = B.load()
+    w = B.MoeWeights()
+    st = lib.moe_expert_ffn(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, None, FAKE, 128, FAKE, FAKE,
+                            FAKE * 16, 1 << 40, None)
+    assert st == B.MOE_ERR_INVALID_ARG and "w_gate" in B.moe_last_error()
+    c.num_experts_per_tok = 33
+    st = lib.moe_expert_ffn(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, None, FAKE, 128, FAKE, FAKE,
+                            FAKE * 16, 1 << 40, None)
+    assert st == B.MOE_ERR_INVALID_ARG and "1..32" in B.moe_last_error()
+
+
+def test_dispatch_counts_follow_the_global_batch():
+    """Rows per local expert average T * ep_size * k / (E * ep_size) = T*k/E."""
+    wl = gen.WORKLOADS["k2_ep8_rank_bf16"]
+    c = gen.gen_dispatch_counts(wl)
+    assert c.shape == (48,)
+    assert abs(c.mean() - 128 * 8 * 8 / 384) < 3
+    assert (gen.gen_dispatch_counts(wl) == c).all()

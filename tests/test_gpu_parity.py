@@ -28,7 +28,11 @@ def small_case(wl, T):
 
 SMALL = [
     (W["tiny_fp32"], 16), (W["tiny_fp32"], 1), (W["tiny_fp32"], 37),
-    (W["small_bf16"], 1), (W["small_bf16"], 7), (W["small_bf16"], 100), (W["small_bf16"], 300),
+    # 1, 7, 40, 100, 300 tokens: streamed work items of 16, 16, 32, 64, 64
+    # rows; 1024 and 1100 tokens: the LDS-tiled kernels (ragged last tiles)
+    (W["small_bf16"], 1), (W["small_bf16"], 7), (W["small_bf16"], 40), (W["small_bf16"], 100),
+    (W["small_bf16"], 300), (W["small_bf16"], 1024),
+    (W["small_bf16"].replace(name="small_bf16_e64", n_routed_experts=64), 1100),
     (W["small_grouped_bf16"], 100),
     (W["small_bf16"].replace(name="small_bf16_hot", bias="hot"), 300),
     (W["small_bf16"].replace(name="small_bf16_noshared", n_shared_experts=0), 50),
@@ -241,3 +245,31 @@ def test_dsv3_grouped_decode_full_size(k2_weights, T):
     check_route(ids, w, route)
     if T in (8, 512):
         check_sampled(wl, case, out, [T - 1])
+
+
+@pytest.mark.parametrize("name", ["k2_ep128_rank_bf16", "k2_ep8_rank_bf16"])
+def test_ep_rank_share_full_size(name):
+    """One expert-parallel rank's share of the Kimi-K2 layer at decode (3 or
+    48 local experts + shared, rows dispatched from 128 tokens per rank):
+    moe_expert_ffn with k as the row capacity.  Every dispatched row and every
+    shared row is compared with the oracle; the capacity rows past the last
+    segment keep their sentinel."""
+    wl = W[name]
+    say(f"[case] {name} T={wl.num_tokens} ep_size={wl.ep_size}")
+    case, cap = cases.make_rank_case(wl)
+    cfg = B.MoeConfig.from_fields(dict(wl.fields(), num_experts_per_tok=cap))
+    T, H = wl.num_tokens, wl.hidden_size
+    R = int(case["offsets"][-1])
+    say(f"  rows {R} (capacity {T * cap}), per expert {case['offsets'].diff().tolist()[:8]}...")
+    sentinel = torch.tensor(1234.0, dtype=torch.bfloat16)
+    y = torch.full((T * cap, H), sentinel.item(), dtype=torch.bfloat16, device="cuda")
+    y_sh = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = B.alloc_workspace(cfg, T)
+    B.moe_expert_ffn(cfg, B.MoeWeights.from_tensors(case), case["x"], case["x_rows"], None, case["offsets"],
+                     y, y_sh, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y[R:] == sentinel.to("cuda"))
+    ref, ref_sh = cases.oracle_rank_share(wl, case)
+    err, err_sh = rel_err(y[:R], ref), rel_err(y_sh, ref_sh)
+    say(f"  rel err routed {err:.3e} shared {err_sh:.3e}")
+    assert err <= TOL[wl.weight_dtype] and err_sh <= TOL[wl.weight_dtype]
