@@ -17,10 +17,15 @@
 // whole 160 KB LDS).  Rows are unpadded; 16-byte slot = chunk ^ ((row >> 1)
 // & 7), because with 128-byte rows the 64 banks give bank group 8*(row%2) +
 // slot and a 128-bit read serves 16 lanes per cycle, so any 16 consecutive
-// rows land in distinct groups.  A K step: all fragments of the step read
-// from LDS, then the next step's 20 DMA issues interleaved with the 64
-// MFMAs (3 : 1), then wait + barrier.  The grouped rows are gathered by the
-// DMA itself through the row -> token map.
+// rows land in distinct groups.  The grouped rows are gathered by the DMA
+// itself through the row -> token map.
+// A K step is 4 sub-steps of 16 K-elements (16 MFMAs each per wave); the
+// fragments of sub-step i+1 are read from LDS while sub-step i computes, and
+// the 20 DMA issues of the next step are spread over the first three
+// sub-steps; then wait + barrier.  The two stages are separate __shared__
+// objects and the step loop is unrolled by two, so the compiler can see that
+// the DMA into one stage never aliases the reads of the other and places no
+// wait for it in front of them.
 //
 // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs.  The
 // (slab, tile) pairs are numbered slab-major and cut into 8 contiguous
@@ -37,7 +42,6 @@ constexpr int kBW = 512;                      // weight rows per slab
 constexpr int kBK = 64;                       // K elements per step
 constexpr int kRowB = 128;                    // bytes per LDS row (kBK bf16)
 constexpr int kStage = (kBW + kBM) * kRowB;   // 80 KB
-constexpr int kSmem = 2 * kStage;
 constexpr int kXcd = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -61,7 +65,10 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
 // MODE 1: down    (K = F or Fs, slab = 512 output rows)
 template <int MODE>
 __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // two stages as separate objects: the compiler then knows that a DMA into
+  // one stage does not alias LDS reads of the other
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
   // ---- XCD-chunked mapping of this block to (slab, tile) ----
   const int ntile = *a.tile_count;
   const int total = slabs * ntile;
@@ -122,17 +129,17 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs) {
     xb[i] = reinterpret_cast<const uint8_t*>(base) + dch[i & 1] * 16;
   }
 
-  auto issue = [&](int s, int buf) {
-    uint8_t* st = smem + buf * kStage;
+  // DMA instruction g (0..19) of step s into stage st: 0-15 weight rows
+  // (8 groups of 8 rows x 2 halves), 16-19 grouped rows
+  auto dma = [&](int g, int s, uint8_t* st) {
     const int64_t ko = static_cast<int64_t>(s) * kRowB;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t o = i * rstride8 + ko + dch[i & 1] * 16;
-      dma16(wb[0] + o, st + (128 * wave + 8 * i) * kRowB);
-      dma16(wb[1] + o, st + (128 * wave + 64 + 8 * i) * kRowB);
+    if (g < 16) {
+      const int i = g >> 1, hf = g & 1;
+      dma16(wb[hf] + i * rstride8 + ko + dch[i & 1] * 16, st + (128 * wave + 64 * hf + 8 * i) * kRowB);
+    } else {
+      const int i = g - 16;
+      dma16(xb[i] + ko, st + (kBW + 32 * wave + 8 * i) * kRowB);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(xb[i] + ko, st + (kBW + 32 * wave + 8 * i) * kRowB);
   };
 
   f32x16 acc[4][4];
@@ -143,47 +150,62 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
 
-  const int steps = K / kBK;
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  const int steps = K / kBK;   // even (K is a multiple of 128)
   const int sw = (r32 >> 1) & 7;                       // row swizzle of this lane's rows
   const int arow = (128 * wave + r32) * kRowB;
   const int brow = (kBW + r32) * kRowB;
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    const uint8_t* st = smem + buf * kStage;
-    uint4 af[4][4], bf[4][4];
+  // fragments of sub-step i (16 K-elements) of a step from stage st
+  auto frag = [&](const uint8_t* st, int i, uint4 (&af)[4], uint4 (&bf)[4]) {
+    const int slot = ((kh * 4 + i) ^ sw) * 16;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) af[m] = *reinterpret_cast<const uint4*>(st + arow + 32 * m * kRowB + slot);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) bf[n] = *reinterpret_cast<const uint4*>(st + brow + 32 * n * kRowB + slot);
+  };
+  // one K step: MFMAs on stage rd while the DMA of step sn fills stage wr;
+  // the next sub-step's fragments are read during the current sub-step
+  auto step = [&](const uint8_t* rd, uint8_t* wr, int sn) {
+    uint4 af[2][4], bf[2][4];
+    frag(rd, 0, af[0], bf[0]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int slot = ((kh * 4 + i) ^ sw) * 16;
+      const int c = i & 1;
+      if (i < 3) frag(rd, i + 1, af[c ^ 1], bf[c ^ 1]);
+      if (i < 3) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) af[i][m] = *reinterpret_cast<const uint4*>(st + arow + 32 * m * kRowB + slot);
-#pragma unroll
-      for (int n = 0; n < 4; ++n) bf[i][n] = *reinterpret_cast<const uint4*>(st + brow + 32 * n * kRowB + slot);
-    }
-    // the fragments must be in registers before the DMA is issued (a wait
-    // for LDS reads placed after it would also wait for the DMA)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    // unconditional, so it shares a basic block with the MFMAs: the last step
-    // re-loads its own (in-bounds) data into the buffer nobody reads again
-    issue(min(s + 1, steps - 1), buf ^ 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int g = 0; g < 7; ++g)
+          if (7 * i + g < 20) dma(7 * i + g, sn, wr);
+      }
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = mma32(af[i][m], bf[i][n], acc[m][n]);
-    // 20 DMA issues spread over the 64 MFMAs: 3 MFMA, 1 memory op, ...
+        for (int n = 0; n < 4; ++n) acc[m][n] = mma32(af[c][m], bf[c][n], acc[m][n]);
+      // 16 MFMAs; in between the next fragments' 8 LDS reads, then the DMAs
+      if (i < 3) {
 #pragma unroll
-    for (int g = 0; g < 20; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        for (int g = 0; g < 8; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        const int nd = i < 2 ? 7 : 6;
+        for (int g = 0; g < nd; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+#pragma unroll
+  for (int g = 0; g < 20; ++g) dma(g, 0, st0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int s = 0; s < steps; s += 2) {
+    step(st0, st1, s + 1);
+    step(st1, st0, min(s + 2, steps - 1));
   }
 
   // ---- epilogue: lane holds rows 8*(i/4) + 4*kh + (i%4) of each 32-row
@@ -235,12 +257,8 @@ bool tile_shapes_ok(int H, int F, int Fs) {
 
 template <int MODE>
 static hipError_t launch_tile(const FfnArgs& a, int slabs, hipStream_t st) {
-  // the 160 KB of LDS exceed the default per-launch limit; raising it once is enough
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&ffn_tile_bf16<MODE>), hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
-  if (attr != hipSuccess) return attr;
   const int64_t blocks = static_cast<int64_t>(slabs) * a.tile_bound;
-  hipLaunchKernelGGL((ffn_tile_bf16<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256), kSmem, st, a,
+  hipLaunchKernelGGL((ffn_tile_bf16<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
                      slabs);
   return hipGetLastError();
 }

@@ -5,7 +5,8 @@
 //
 // Same data movement as the bf16 tile kernel: both operands go global -> LDS
 // by DMA (global_load_lds_dwordx4), 128-byte unpadded LDS rows with the slot
-// swizzle chunk ^ ((row >> 1) & 7), two stages, the next step's DMA issues
+// swizzle chunk ^ ((row >> 1) & 7), two stages held in separate __shared__
+// objects, the next step's DMA issues and the next row-tile's LDS reads
 // interleaved with the MFMAs, XCD-chunked (slab, tile) order.  A 128-byte
 // row is 128 fp8 K-elements: exactly one quantisation block per K step, so
 // each step is two v_mfma_scale_f32_32x32x64_f8f6f4 (unit e8m0 scales) per
@@ -26,7 +27,6 @@ constexpr int kBM = 128;                      // grouped rows per work item
 constexpr int kBW = 256;                      // weight rows per slab
 constexpr int kRowB = 128;                    // bytes per LDS row = K elements per step
 constexpr int kStage = (kBW + kBM) * kRowB;   // 48 KB
-constexpr int kSmem = 2 * kStage;
 constexpr int kXcd = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -53,7 +53,10 @@ __device__ __forceinline__ f32x16 mma_fp8_32(const uint4& a0, const uint4& a1, c
 // MODE 1: down    (K = F or Fs; slab = 256 output rows)
 template <int MODE>
 __global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // two stages as separate objects (no alias between a DMA into one and the
+  // LDS reads of the other, as in the bf16 tile kernel)
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
   const int ntile = *a.tile_count;
   const int total = slabs * ntile;
   const int per = (total + kXcd - 1) / kXcd;
@@ -134,14 +137,11 @@ __global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
     }
   }
 
-  auto issue = [&](int s, int buf) {
-    uint8_t* st = smem + buf * kStage;
+  // DMA instruction g (0..11) of step s into stage st: 0-7 weight rows, 8-11 grouped rows
+  auto dma = [&](int g, int s, uint8_t* st) {
     const int64_t ko = static_cast<int64_t>(s) * kRowB;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dma16(wdma + i * rstride8 + ko + dch[i & 1] * 16, st + (64 * wave + 8 * i) * kRowB);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(xb[i] + ko, st + (kBW + 32 * wave + 8 * i) * kRowB);
+    if (g < 8) dma16(wdma + g * rstride8 + ko + dch[g & 1] * 16, st + (64 * wave + 8 * g) * kRowB);
+    else dma16(xb[g - 8] + ko, st + (kBW + 32 * wave + 8 * (g - 8)) * kRowB);
   };
 
   f32x16 acc[4][2];
@@ -153,56 +153,73 @@ __global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
       for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
 
   const int steps = static_cast<int>(KB);
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   const int sw = (r32 >> 1) & 7;
   const int arow = (128 * wm + r32) * kRowB;
   const int brow = (kBW + 64 * wn + r32) * kRowB;
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    const uint8_t* st = smem + buf * kStage;
-    // fragments: MFMA i (0, 1) takes chunks kh*4 + 2i and kh*4 + 2i + 1
-    uint4 af[4][4], bf[2][4];
+  // fragments of one 32-row tile: MFMA i (0, 1) takes chunks kh*4 + 2i, +1
+  auto frag = [&](const uint8_t* st, int row, uint4 (&f)[4]) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int slot = ((kh * 4 + c) ^ sw) * 16;
+    for (int c = 0; c < 4; ++c) f[c] = *reinterpret_cast<const uint4*>(st + row + (((kh * 4 + c) ^ sw) * 16));
+  };
+  // scales of the step being computed (loaded one step ahead)
+  float ws[2], rs[2];
+  auto scales = [&](int s, float (&w)[2], float (&r)[2]) {
+    w[0] = wsc[0][s];
+    w[1] = wsc[1][s];
+    r[0] = rsc[0][s];
+    r[1] = rsc[1][s];
+  };
+  // one K step (one 128-wide quantisation block): the weight row-tiles m = 0..3
+  // in turn, the next one's fragments read while the current one computes,
+  // three of the next step's 12 DMA issues per row-tile
+  auto step = [&](const uint8_t* rd, uint8_t* wr, int sn) {
+    float nws[2], nrs[2];
+    scales(sn, nws, nrs);
+    uint4 bf[2][4], af[2][4];
+    frag(rd, brow, bf[0]);
+    frag(rd, brow + 32 * kRowB, bf[1]);
+    frag(rd, arow, af[0]);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) af[m][c] = *reinterpret_cast<const uint4*>(st + arow + 32 * m * kRowB + slot);
+    for (int m = 0; m < 4; ++m) {
+      const int c = m & 1;
+      if (m < 3) frag(rd, arow + 32 * (m + 1) * kRowB, af[c ^ 1]);
 #pragma unroll
-      for (int n = 0; n < 2; ++n) bf[n][c] = *reinterpret_cast<const uint4*>(st + brow + 32 * n * kRowB + slot);
-    }
-    float ws[2], rs[2];
-    ws[0] = wsc[0][s];
-    ws[1] = wsc[1][s];
-    rs[0] = rsc[0][s];
-    rs[1] = rsc[1][s];
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    issue(min(s + 1, steps - 1), buf ^ 1);
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int g = 0; g < 3; ++g) dma(3 * m + g, sn, wr);
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         f32x16 p;
 #pragma unroll
         for (int i = 0; i < 16; ++i) p[i] = 0.f;
-        p = mma_fp8_32(af[m][0], af[m][1], bf[n][0], bf[n][1], p);
-        p = mma_fp8_32(af[m][2], af[m][3], bf[n][2], bf[n][3], p);
+        p = mma_fp8_32(af[c][0], af[c][1], bf[n][0], bf[n][1], p);
+        p = mma_fp8_32(af[c][2], af[c][3], bf[n][2], bf[n][3], p);
         // gate_up: m = 0, 1 are gate rows, 2, 3 up rows; down: one block
         const float sc = (m < 2 ? ws[0] : ws[1]) * rs[n];
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[m][n][i] = fmaf(p[i], sc, acc[m][n][i]);
       }
-#pragma unroll
-    for (int g = 0; g < 12; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    ws[0] = nws[0];
+    ws[1] = nws[1];
+    rs[0] = nrs[0];
+    rs[1] = nrs[1];
+  };
+
+  scales(0, ws, rs);
+#pragma unroll
+  for (int g = 0; g < 12; ++g) dma(g, 0, st0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // steps in pairs (stage 0 then 1); a step past the end re-loads the last
+  // step's (in-bounds) data into the stage nobody reads again
+  int s = 0;
+  for (; s + 1 < steps; s += 2) {
+    step(st0, st1, s + 1);
+    step(st1, st0, min(s + 2, steps - 1));
   }
+  if (s < steps) step(st0, st1, s);
 
   // ---- epilogue: lane holds weight rows 8*(i/4) + 4*kh + (i%4) of each
   // 32-row sub-tile, for grouped row 64*wn + 32*n + r32 ----
@@ -252,11 +269,8 @@ bool tile_fp8_shapes_ok(int H, int F, int Fs) {
 
 template <int MODE>
 static hipError_t launch_tile_fp8(const FfnArgs& a, int slabs, hipStream_t st) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&ffn_tile_fp8<MODE>), hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
-  if (attr != hipSuccess) return attr;
   const int64_t blocks = static_cast<int64_t>(slabs) * a.tile_bound;
-  hipLaunchKernelGGL((ffn_tile_fp8<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256), kSmem, st, a,
+  hipLaunchKernelGGL((ffn_tile_fp8<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
                      slabs);
   return hipGetLastError();
 }
