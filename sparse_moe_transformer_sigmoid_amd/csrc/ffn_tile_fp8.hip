@@ -13,8 +13,7 @@
 // 32x32 output tile into a fresh partial, added to the fp32 accumulator
 // scaled by weight-block scale x row scale:
 //   acc += (sum_k q_w q_a) * s_w[block][kb] * s_a[row][kb].
-// The partials need registers next to the accumulators, so the block is 256
-// weight rows x 128 grouped rows, 4 waves of 128 x 64.
+// The block is 256 weight rows x 128 grouped rows in 8 waves of 64 x 64.
 // gate_up writes the SwiGLU output in fp32 (re-quantised per row and 128
 // channels before the down projection); down writes bf16.
 #include "kernels.h"
@@ -26,14 +25,27 @@ namespace {
 constexpr int kBM = 128;                      // grouped rows per work item
 constexpr int kBW = 256;                      // weight rows per slab
 constexpr int kRowB = 128;                    // bytes per LDS row = K elements per step
-constexpr int kStage = (kBW + kBM) * kRowB;   // 48 KB
+constexpr int kData = (kBW + kBM) * kRowB;    // 48 KB of operands per stage
+constexpr int kStage = kData + 8 * 64 * 4;     // + grouped-row scales: 64 slots per wave
+constexpr int kMaxKB = 64;                     // K blocks (K <= 8192) of the weight-scale table
 constexpr int kXcd = 8;
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef __attribute__((address_space(1))) void* glb_ptr;
-
-__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds((glb_ptr)(g), (lds_ptr)(l), 16, 0, 0);
+// Global -> LDS DMA issued from inline asm, so that the compiler neither
+// tracks it nor places its own (full) waits for it: every wait on these
+// loads is an explicit s_waitcnt vmcnt(n) below.  The instruction has no
+// register result (lane i writes 16 or 4 bytes at LDS address m0 + 16 i or
+// m0 + 4 i); its address operand is read at issue.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0v), "v"(g) : "memory", "m0");
+}
+// LDS byte address of a __shared__ object (an address-space cast)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(p)));
 }
 
 __device__ __forceinline__ f32x16 mma_fp8_32(const uint4& a0, const uint4& a1, const uint4& b0,
@@ -51,12 +63,18 @@ __device__ __forceinline__ f32x16 mma_fp8_32(const uint4& a0, const uint4& a1, c
 
 // MODE 0: gate_up (K = H; slab = 128 features = 128 gate + 128 up rows)
 // MODE 1: down    (K = F or Fs; slab = 256 output rows)
+// 8 waves, two per SIMD: wave (wm, wn) owns LDS weight rows 64*wm + [0, 64)
+// (gate_up: 32 gate then 32 up rows of features o0 + 32*wm + [0, 32)) and
+// grouped rows 64*wn + [0, 64); while one wave of a SIMD applies the scales
+// of its partial products (VALU), the other's MFMAs run.
 template <int MODE>
-__global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
+__global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
   // two stages as separate objects (no alias between a DMA into one and the
   // LDS reads of the other, as in the bf16 tile kernel)
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[kStage];
+  __shared__ float wscale[4][2][kMaxKB];        // [wm][gate/up or down][K block]
   const int ntile = *a.tile_count;
   const int total = slabs * ntile;
   const int per = (total + kXcd - 1) / kXcd;
@@ -69,16 +87,16 @@ __global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
   const int Fg = sh ? a.Fs : a.F;
   const int64_t TK = static_cast<int64_t>(a.T) * a.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;        // 128 weight rows x 64 grouped rows
+  const int wm = wave >> 1, wn = wave & 1;        // 64 weight rows x 64 grouped rows
   const int r32 = lane & 31, kh = lane >> 5;
   const int drow = lane >> 3;
   const int dch[2] = {(lane & 7) ^ ((drow >> 1) & 7), (lane & 7) ^ ((4 + (drow >> 1)) & 7)};
 
-  // ---- weight rows: LDS rows 128*wm + [0, 128); this wave's DMA covers
-  // LDS rows 64*wave + [0, 64) (8 instructions of 8 rows) ----
+  // ---- weights: this wave's DMA fills LDS rows 32*wave + [0, 32) (4
+  // instructions of 8 rows); the compute side reads rows 64*wm + [0, 64) ----
   int K, o0;
-  const uint8_t* wdma;               // first weight row of this wave's DMA share
-  const float* wsc[2];               // scale rows of the wave's two 64-row halves (compute side)
+  const uint8_t* wdma;
+  const float* wsc[2];               // scale rows of the wave's two 32-row tiles
   int64_t KB;
   if (MODE == 0) {
     K = a.H;
@@ -88,11 +106,10 @@ __global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
     const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.F * a.H;
     const uint8_t* wg = static_cast<const uint8_t*>(sh ? a.sh_gate : a.w_gate) + wofs;
     const uint8_t* wu = static_cast<const uint8_t*>(sh ? a.sh_up : a.w_up) + wofs;
-    // LDS rows 128 q + [0, 64) = gate features o0 + 64 q + ., + [64, 128) = up
+    // LDS rows 64 q + [0, 32) = gate features o0 + 32 q + ., + [32, 64) = up
     const int q = wave >> 1, half = wave & 1;
-    wdma = (half ? wu : wg) + static_cast<int64_t>(o0 + 64 * q + drow) * K;
-    const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.F / 128) * KB) +
-                         static_cast<int64_t>((o0 + 64 * wm) / 128) * KB;
+    wdma = (half ? wu : wg) + static_cast<int64_t>(o0 + 32 * q + drow) * K;
+    const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.F / 128) * KB) + ((o0 + 32 * wm) / 128) * KB;
     wsc[0] = (sh ? a.sh_s_gate : a.s_gate) + sofs;
     wsc[1] = (sh ? a.sh_s_up : a.s_up) + sofs;
   } else {
@@ -101,17 +118,16 @@ __global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
     o0 = slab * kBW;
     const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.H * a.F;
     const uint8_t* wd = static_cast<const uint8_t*>(sh ? a.sh_down : a.w_down) + wofs;
-    wdma = wd + static_cast<int64_t>(o0 + 64 * wave + drow) * K;
-    const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.H / 128) * KB) +
-                         static_cast<int64_t>((o0 + 128 * wm) / 128) * KB;
+    wdma = wd + static_cast<int64_t>(o0 + 32 * wave + drow) * K;
+    const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.H / 128) * KB) + ((o0 + 64 * wm) / 128) * KB;
     wsc[0] = wsc[1] = (sh ? a.sh_s_down : a.s_down) + sofs;
   }
   const int64_t rstride8 = static_cast<int64_t>(8) * K;
-  // ---- grouped rows: this wave's DMA covers LDS rows kBW + 32*wave + [0, 32) ----
-  const uint8_t* xb[4];
+  // ---- grouped rows: this wave's DMA fills LDS rows kBW + 16*wave + [0, 16) ----
+  const uint8_t* xb[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tr = 32 * wave + 8 * i + drow;
+  for (int i = 0; i < 2; ++i) {
+    const int tr = 16 * wave + 8 * i + drow;
     const int64_t p = tl.row0 + min(tr, tl.rows - 1);
     const uint8_t* base;
     if (MODE == 0) {
@@ -123,30 +139,42 @@ __global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
     }
     xb[i] = base + dch[i & 1] * 16;
   }
-  // ---- row scales of this lane's two grouped rows (compute side) ----
-  const float* rsc[2];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int tr = 64 * wn + 32 * n + r32;
+  // ---- weight-block scales of the four 64-row groups, all K blocks, into
+  // LDS once (read there at every step) ----
+  if (wn == 0)
+    for (int i = lane; i < 2 * KB; i += 64) wscale[wm][i / KB][i % KB] = wsc[i / KB][i % KB];
+  // ---- row scales: lane l of this wave copies the scale of grouped row
+  // 16*wave + l % 16 for each step into the stage's 64 slots of the wave
+  // (kData + 256 * wave + 4 * l; the compute side reads l < 16) ----
+  const float* rsd;
+  {
+    const int tr = 16 * wave + (lane & 15);
     const int64_t p = tl.row0 + min(tr, tl.rows - 1);
     if (MODE == 0) {
-      if (sh) rsc[n] = a.xs_scales + (p - TK) * KB;
-      else rsc[n] = a.xr_scales + (a.xr_rows ? a.xr_rows[p] : p) * KB;
+      if (sh) rsd = a.xs_scales + (p - TK) * KB;
+      else rsd = a.xr_scales + (a.xr_rows ? a.xr_rows[p] : p) * KB;
     } else {
-      rsc[n] = sh ? a.h_sh_scales + (p - TK) * KB : a.h_scales + p * KB;
+      rsd = sh ? a.h_sh_scales + (p - TK) * KB : a.h_scales + p * KB;
     }
   }
 
-  // DMA instruction g (0..11) of step s into stage st: 0-7 weight rows, 8-11 grouped rows
-  auto dma = [&](int g, int s, uint8_t* st) {
+  // the 7 DMA issues of step s into stage st: 4 x 8 weight rows, 2 x 8
+  // grouped rows, then the 16 row scales
+  auto dma = [&](int g, int s, const uint8_t* st) {
     const int64_t ko = static_cast<int64_t>(s) * kRowB;
-    if (g < 8) dma16(wdma + g * rstride8 + ko + dch[g & 1] * 16, st + (64 * wave + 8 * g) * kRowB);
-    else dma16(xb[g - 8] + ko, st + (kBW + 32 * wave + 8 * (g - 8)) * kRowB);
+    const uint32_t l = lds_addr(st);
+    if (g < 4) {
+      dma16(wdma + g * rstride8 + ko + dch[g & 1] * 16, l + (32 * wave + 8 * g) * kRowB);
+    } else if (g < 6) {
+      dma16(xb[g - 4] + ko, l + (kBW + 16 * wave + 8 * (g - 4)) * kRowB);
+    } else {
+      dma4(rsd + s, l + kData + 256 * wave);
+    }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
@@ -154,75 +182,81 @@ __global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
 
   const int steps = static_cast<int>(KB);
   const int sw = (r32 >> 1) & 7;
-  const int arow = (128 * wm + r32) * kRowB;
+  const int arow = (64 * wm + r32) * kRowB;
   const int brow = (kBW + 64 * wn + r32) * kRowB;
+  // grouped row r = 64 wn + 32 n + r32 has its scale at kData + 256 (r / 16) + 4 (r % 16)
+  const int srow = kData + 256 * (4 * wn + (r32 >> 4)) + 4 * (r32 & 15);
   // fragments of one 32-row tile: MFMA i (0, 1) takes chunks kh*4 + 2i, +1
   auto frag = [&](const uint8_t* st, int row, uint4 (&f)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) f[c] = *reinterpret_cast<const uint4*>(st + row + (((kh * 4 + c) ^ sw) * 16));
   };
-  // scales of the step being computed (loaded one step ahead)
-  float ws[2], rs[2];
-  auto scales = [&](int s, float (&w)[2], float (&r)[2]) {
-    w[0] = wsc[0][s];
-    w[1] = wsc[1][s];
-    r[0] = rsc[0][s];
-    r[1] = rsc[1][s];
-  };
-  // one K step (one 128-wide quantisation block): the weight row-tiles m = 0..3
-  // in turn, the next one's fragments read while the current one computes,
-  // three of the next step's 12 DMA issues per row-tile
-  auto step = [&](const uint8_t* rd, uint8_t* wr, int sn) {
-    float nws[2], nrs[2];
-    scales(sn, nws, nrs);
-    uint4 bf[2][4], af[2][4];
+  // One K step s (one 128-wide quantisation block) on stage rd while the DMA
+  // of step sd (= s + 2, clamped) fills stage wr: the four 32x32 tiles t =
+  // (m, n), the partial product of tile t+1 computed before tile t's is
+  // scaled into the accumulator (MFMA and VALU work overlap).
+  auto step = [&](const uint8_t* rd, const uint8_t* wr, int s, int sd) {
+    const float ws[2] = {wscale[wm][0][s], wscale[wm][1][s]};
+    const float rs[2] = {*reinterpret_cast<const float*>(rd + srow),
+                         *reinterpret_cast<const float*>(rd + srow + 512)};
+    uint4 af[2][4], bf[2][4];
+    frag(rd, arow, af[0]);
+    frag(rd, arow + 32 * kRowB, af[1]);
     frag(rd, brow, bf[0]);
     frag(rd, brow + 32 * kRowB, bf[1]);
-    frag(rd, arow, af[0]);
+    f32x16 p[2];
+    auto part = [&](int t) {
+      const int m = t >> 1, n = t & 1;
+      f32x16 z;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int c = m & 1;
-      if (m < 3) frag(rd, arow + 32 * (m + 1) * kRowB, af[c ^ 1]);
+      for (int i = 0; i < 16; ++i) z[i] = 0.f;
+      z = mma_fp8_32(af[m][0], af[m][1], bf[n][0], bf[n][1], z);
+      p[t & 1] = mma_fp8_32(af[m][2], af[m][3], bf[n][2], bf[n][3], z);
+    };
+    auto fold = [&](int t) {
+      const int m = t >> 1, n = t & 1;
+      // gate_up: m = 0 gate rows, 1 up rows; down: one block
+      const float sc = ws[m] * rs[n];
 #pragma unroll
-      for (int g = 0; g < 3; ++g) dma(3 * m + g, sn, wr);
+      for (int i = 0; i < 16; ++i) acc[m][n][i] = fmaf(p[t & 1][i], sc, acc[m][n][i]);
+    };
+    part(0);
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        f32x16 p;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = 0.f;
-        p = mma_fp8_32(af[c][0], af[c][1], bf[n][0], bf[n][1], p);
-        p = mma_fp8_32(af[c][2], af[c][3], bf[n][2], bf[n][3], p);
-        // gate_up: m = 0, 1 are gate rows, 2, 3 up rows; down: one block
-        const float sc = (m < 2 ? ws[0] : ws[1]) * rs[n];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[m][n][i] = fmaf(p[i], sc, acc[m][n][i]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int t = 0; t < 4; ++t) {
+      if (t < 3) part(t + 1);
+      dma(2 * t, sd, wr);
+      if (t < 3) dma(2 * t + 1, sd, wr);
+      fold(t);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    ws[0] = nws[0];
-    ws[1] = nws[1];
-    rs[0] = nrs[0];
-    rs[1] = nrs[1];
+    // this wave's DMA of step s + 1 has landed once at most the 7 issued
+    // during this step are outstanding; this wave's LDS reads are done
+    // (lgkmcnt); then the barrier.  (__syncthreads would also wait for the
+    // DMA of step s + 2.)
+    asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
-  scales(0, ws, rs);
 #pragma unroll
-  for (int g = 0; g < 12; ++g) dma(g, 0, st0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  // steps in pairs (stage 0 then 1); a step past the end re-loads the last
-  // step's (in-bounds) data into the stage nobody reads again
+  for (int g = 0; g < 7; ++g) dma(g, 0, st0);
+#pragma unroll
+  for (int g = 0; g < 7; ++g) dma(g, min(1, steps - 1), st1);
+  // (lgkmcnt: the weight-scale table written above is visible after the barrier)
+  asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // steps in threes (stages 0, 1, 2); a DMA index past the end re-loads the
+  // last step's (in-bounds) data into a stage nobody reads again
+  const int last = steps - 1;
   int s = 0;
-  for (; s + 1 < steps; s += 2) {
-    step(st0, st1, s + 1);
-    step(st1, st0, min(s + 2, steps - 1));
+  for (; s + 2 < steps; s += 3) {
+    step(st0, st2, s, min(s + 2, last));
+    step(st1, st0, s + 1, min(s + 3, last));
+    step(st2, st1, s + 2, min(s + 4, last));
   }
-  if (s < steps) step(st0, st1, s);
+  if (s < steps) step(st0, st2, s, min(s + 2, last));
+  if (s + 1 < steps) step(st1, st0, s + 1, min(s + 3, last));
+  // no DMA may still be writing LDS when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: lane holds weight rows 8*(i/4) + 4*kh + (i%4) of each
-  // 32-row sub-tile, for grouped row 64*wn + 32*n + r32 ----
+  // 32-row tile, for grouped row 64*wn + 32*n + r32 ----
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int tr = 64 * wn + 32 * n + r32;
@@ -230,24 +264,22 @@ __global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
     const int64_t p = tl.row0 + tr;
     if (MODE == 0) {
       float* dst = sh ? static_cast<float*>(a.h_sh) + (p - TK) * a.Fs : static_cast<float*>(a.h) + p * a.F;
-      dst += o0 + 64 * wm + 4 * kh;
+      dst += o0 + 32 * wm + 4 * kh;
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float4 h;
-          h.x = silu(acc[m][n][4 * g + 0]) * acc[m + 2][n][4 * g + 0];
-          h.y = silu(acc[m][n][4 * g + 1]) * acc[m + 2][n][4 * g + 1];
-          h.z = silu(acc[m][n][4 * g + 2]) * acc[m + 2][n][4 * g + 2];
-          h.w = silu(acc[m][n][4 * g + 3]) * acc[m + 2][n][4 * g + 3];
-          *reinterpret_cast<float4*>(dst + 32 * m + 8 * g) = h;
-        }
+      for (int g = 0; g < 4; ++g) {
+        float4 h;
+        h.x = silu(acc[0][n][4 * g + 0]) * acc[1][n][4 * g + 0];
+        h.y = silu(acc[0][n][4 * g + 1]) * acc[1][n][4 * g + 1];
+        h.z = silu(acc[0][n][4 * g + 2]) * acc[1][n][4 * g + 2];
+        h.w = silu(acc[0][n][4 * g + 3]) * acc[1][n][4 * g + 3];
+        *reinterpret_cast<float4*>(dst + 8 * g) = h;
+      }
     } else {
       uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (p - TK) * a.H
                          : static_cast<uint16_t*>(a.y) + p * a.H;
-      dst += o0 + 128 * wm + 4 * kh;
+      dst += o0 + 64 * wm + 4 * kh;
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           uint2 v2;
@@ -263,14 +295,17 @@ __global__ __launch_bounds__(256) void ffn_tile_fp8(FfnArgs a, int slabs) {
 
 int tile_fp8_rows() { return kBM; }
 
+// slabs must divide the weight dimensions, and every K fits the LDS table of
+// weight-block scales
 bool tile_fp8_shapes_ok(int H, int F, int Fs) {
-  return F % (kBW / 2) == 0 && Fs % (kBW / 2) == 0 && H % kBW == 0;
+  return F % (kBW / 2) == 0 && Fs % (kBW / 2) == 0 && H % kBW == 0 && H <= 128 * kMaxKB &&
+         F <= 128 * kMaxKB && Fs <= 128 * kMaxKB;
 }
 
 template <int MODE>
 static hipError_t launch_tile_fp8(const FfnArgs& a, int slabs, hipStream_t st) {
   const int64_t blocks = static_cast<int64_t>(slabs) * a.tile_bound;
-  hipLaunchKernelGGL((ffn_tile_fp8<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+  hipLaunchKernelGGL((ffn_tile_fp8<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, a,
                      slabs);
   return hipGetLastError();
 }
