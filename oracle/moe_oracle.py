@@ -39,9 +39,17 @@ What it computes, with where the pages fix each step:
    s = fp32(amax) / 448 (fp32 divide; s = 1 for an all-zero group),
    q = RNE-saturate-e4m3fn(fp32(v) / s), and used as q * s.  The router stays
    unquantised.
+10. The sub-block around the layer (block_forward): the pre-MoE RMSNorm
+   u = x / sqrt(mean(x^2) + eps) * g, rounded once to the activation dtype
+   (the layer's input, as in a plain norm-then-linear model), and the residual
+   add out = x + layer(u).  ["Kimi K2 Base" architecture table: RMSNorm;
+   raw config fields: rms_norm_eps 1e-06.]  The norm and the rounding
+   decision are fp64 here and in the kernel, so both sides round the same
+   value.
 
 Everything is float64 except the two places where the method itself fixes
-fp32 (the fp8 scale and the division feeding the e4m3 rounding).
+fp32 (the fp8 scale and the division feeding the e4m3 rounding) and the one
+rounding of the normalised activations to the activation dtype (step 10).
 
 Pins: each function is checked by tests against page-printed values, closed
 forms, library routines or brute force (tests/test_oracle_pins.py).  Parity
@@ -286,3 +294,60 @@ def layer_forward(x, router_w, router_bias, expert: ExpertFn, shared: Optional[S
         y = swiglu_expert(x[rows], *expert(int(e)), fp8_act=fp8_act)
         out[rows] += r.weights[rows, slot][:, None] * y
     return out, r
+
+
+# --------------------------------------------------------------------------
+# the sub-block around the layer: pre-MoE RMSNorm and residual add
+# ("Kimi K2 Base" architecture table: RMSNorm; raw config fields:
+# rms_norm_eps 1e-06)
+# --------------------------------------------------------------------------
+def round_bf16(v) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even) of fp64 values, returned as fp64.
+
+    bfloat16 keeps 7 of the 52 fp64 mantissa bits: the 45 dropped bits are
+    rounded half-to-even straight from fp64 (no detour through fp32, which
+    would round twice).  Defined for zero and for magnitudes in the normal
+    bfloat16 range [2^-126, 2^128)."""
+    a = np.ascontiguousarray(np.asarray(v, np.float64))
+    bits = a.view(np.uint64)
+    sign = bits & np.uint64(1 << 63)
+    mag = bits & np.uint64((1 << 63) - 1)
+    low = mag & np.uint64((1 << 45) - 1)
+    kept = mag >> np.uint64(45)
+    half = np.uint64(1 << 44)
+    up = (low > half) | ((low == half) & ((kept & np.uint64(1)) == np.uint64(1)))
+    kept = kept + up.astype(np.uint64)
+    out = ((kept << np.uint64(45)) | sign).view(np.float64)
+    m = np.abs(out)
+    if not np.all((a == 0) | ((np.abs(a) >= 2.0 ** -126) & (m < 2.0 ** 128))):
+        raise ValueError("round_bf16: value outside the normal bfloat16 range")
+    return out
+
+
+def round_act(v, act_dtype: str) -> np.ndarray:
+    """Round to the activation dtype: "bf16" (round_bf16) or "f32" (IEEE
+    round-to-nearest-even of the fp64 value)."""
+    if act_dtype == "f32":
+        return np.asarray(v, np.float64).astype(np.float32).astype(np.float64)
+    return round_bf16(v)
+
+
+def rms_norm(x, weight, eps: float) -> np.ndarray:
+    """u = x / sqrt(mean_h x^2 + eps) * weight, per row, in fp64."""
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(weight, np.float64)
+
+
+def block_forward(x, norm_weight, eps: float, router_w, router_bias, expert: ExpertFn,
+                  shared: Optional[Sequence[np.ndarray]], *, act_dtype: str = "bf16",
+                  tokens: Optional[np.ndarray] = None, **layer_kw):
+    """out = x + layer(u), u = the activation-dtype rounding of rms_norm(x).
+
+    Returns (out [rows, H] fp64, Route of the computed rows, u [rows, H])."""
+    x = np.asarray(x, np.float64)
+    if tokens is not None:
+        x = x[np.asarray(tokens)]
+    u = round_act(rms_norm(x, norm_weight, eps), act_dtype)
+    y, r = layer_forward(u, router_w, router_bias, expert, shared, **layer_kw)
+    return x + y, r, u

@@ -48,6 +48,7 @@ TID_FP8_U = 11
 TID_ZIPF_RANK = 12
 TID_DISPATCH_COUNT = 13
 TID_DISPATCH_ROWS = 14
+TID_NORM = 15
 
 F32, BF16, FP8 = "f32", "bf16", "fp8_e4m3"
 
@@ -74,6 +75,8 @@ class Workload:
     weight_dtype: str = BF16       # expert weights
     weight_std: float = 0.02
     bias: str = "normal"           # "normal" | "zipf" | "zero" | "hot"
+    rms_norm_eps: float = 1e-6     # pre-MoE RMSNorm ("Kimi K2 Base" raw config fields)
+    norm_weight_std: float = 0.1   # RMSNorm weight ~ 1 + N(0, std)
     bias_std: float = 0.01
     zipf_beta: float = 0.1
     zipf_s: float = 1.1
@@ -270,6 +273,12 @@ def gen_expert_weights(wl: Workload, device="cpu", experts: Optional[range] = No
             if s is not None:
                 out["sh_s_" + name] = s
     return out
+
+
+def gen_norm_weight(wl: Workload) -> torch.Tensor:
+    """RMSNorm weight [H] in the activation dtype: 1 + N(0, norm_weight_std)."""
+    a = 1.0 + _rng(wl.seed, TID_NORM).standard_normal(wl.hidden_size, np.float32) * np.float32(wl.norm_weight_std)
+    return round_to(a, wl.act_dtype)
 
 
 def gen_dispatch_counts(wl: Workload, num_tokens: Optional[int] = None) -> np.ndarray:

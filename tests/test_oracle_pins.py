@@ -430,10 +430,89 @@ def test_fp8_layer_matches_dequantised_reference():
     np.testing.assert_allclose(out, expect, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------- the sub-block: RMSNorm + residual add ----
+# ("Kimi K2 Base" architecture table: RMSNorm; raw config fields: rms_norm_eps)
+def _bf16_neighbours(r):
+    """The bf16 values just below and above a bf16 value r > 0 (one unit in
+    the last of its 8 significant bits)."""
+    _, e = np.frexp(r)             # r = m 2^e, m in [0.5, 1)
+    ulp = np.ldexp(1.0, e - 8)
+    return r - ulp, r + ulp
+
+
+def check_round_bf16(seed=11):
+    # library routine: torch's fp32 -> bf16 cast (round to nearest even) on
+    # values that fp32 holds exactly
+    v = np.random.default_rng(seed).standard_normal(20000).astype(np.float32).astype(np.float64)
+    assert np.array_equal(om.round_bf16(v), torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).double().numpy())
+    # the nearest value by definition, on fp64 values fp32 cannot hold
+    w = np.abs(np.random.default_rng(seed + 1).standard_normal(2000)) + 1e-3
+    r = om.round_bf16(w)
+    lo, hi = _bf16_neighbours(r)
+    assert np.all(np.abs(w - r) <= np.abs(w - lo)) and np.all(np.abs(w - r) <= np.abs(w - hi))
+    # just above the midpoint 1 + 2^-8 of 1 and 1 + 2^-7: rounds up (a detour
+    # through fp32 would land on the midpoint and round to even, i.e. down)
+    assert om.round_bf16(np.array([1.0 + 2.0 ** -8 + 2.0 ** -40]))[0] == 1.0 + 2.0 ** -7
+    # exact midpoints go to the even neighbour
+    assert om.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert om.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+def test_round_bf16_nearest_even_from_fp64():
+    check_round_bf16()
+
+
+def check_rms_norm(seed=12):
+    rng = np.random.default_rng(seed)
+    x, g = rng.standard_normal((5, 64)), 1.0 + 0.1 * rng.standard_normal(64)
+    # library routine: torch's RMSNorm in fp64
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(g), 1e-6).numpy()
+    np.testing.assert_allclose(om.rms_norm(x, g, 1e-6), ref, rtol=1e-14, atol=1e-14)
+    # closed form: a constant row c gives g * c / sqrt(c^2 + eps)
+    c, eps = -3.0, 0.25
+    np.testing.assert_allclose(om.rms_norm(np.full((1, 8), c), np.ones(8), eps), c / math.sqrt(c * c + eps),
+                               rtol=1e-15)
+    # eps = 0: scale-free and of unit mean square
+    u = om.rms_norm(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(om.rms_norm(7.5 * x, np.ones(64), 0.0), u, rtol=1e-14)
+    np.testing.assert_allclose(np.mean(u * u, axis=1), 1.0, rtol=1e-14)
+
+
+def test_rms_norm_matches_torch_and_closed_forms():
+    check_rms_norm()
+
+
+def check_block(seed=13):
+    wl = gen.WORKLOADS["small_bf16"].replace(num_tokens=5, rms_norm_eps=0.0)
+    case = cases.make_case(wl)
+    x = cases.to64(case["x"]) * 3.0
+    g = cases.to64(gen.gen_norm_weight(wl))
+    kw = dict(cases.route_kwargs(wl))
+    ex, sh = cases.expert_fn(wl, case), cases.shared_weights(wl, case)
+    rw, b = cases.to64(case["router_w"]), cases.to64(case["router_bias"])
+    out, r, u = om.block_forward(x, g, 0.0, rw, b, ex, sh, **kw)
+    # the residual: out - x is the layer applied to u, u the bf16 rounding of the norm
+    np.testing.assert_array_equal(u, om.round_bf16(om.rms_norm(x, g, 0.0)))
+    y, _ = om.layer_forward(u, rw, b, ex, sh, **kw)
+    np.testing.assert_allclose(out - x, y, rtol=0, atol=1e-12)
+    # eps = 0: the layer part does not depend on the scale of x
+    out2, _, _ = om.block_forward(0.25 * x, g, 0.0, rw, b, ex, sh, **kw)
+    np.testing.assert_allclose(out2 - 0.25 * x, out - x, rtol=0, atol=1e-12)
+    # all-zero expert weights: only the residual is left
+    zero = tuple(np.zeros_like(m) for m in sh)
+    out3, _, _ = om.block_forward(x, g, 0.0, rw, b, lambda e: zero, zero, **kw)
+    np.testing.assert_array_equal(out3, x)
+
+
+def test_block_is_residual_plus_layer_on_rounded_norm():
+    check_block()
+
+
 # ------------------------------------------------------ planted mistakes ---
 PINS = [check_param_counts, check_routing_worked_example, check_swiglu_worked_example,
         check_bruteforce_topk, check_bruteforce_grouped, check_identical_experts,
-        check_single_expert, check_e4m3, check_permutation]
+        check_single_expert, check_e4m3, check_permutation, check_round_bf16, check_rms_norm,
+        check_block]
 
 
 def _any_pin_fails():
@@ -460,6 +539,16 @@ MUTANTS = {
     "e4m3_truncate": ("e4m3_round", lambda orig: (lambda v: _trunc_e4m3(v))),
     "permute_unstable": ("permute", lambda orig: (lambda ids, E: _unstable_permute(orig, ids, E))),
     "expert_params_two_linears": ("expert_params", lambda orig: (lambda h, f: 2 * h * f)),
+    "bf16_via_fp32": ("round_bf16", lambda orig: (
+        lambda v: torch.from_numpy(np.asarray(v, np.float64).astype(np.float32)).to(torch.bfloat16).double().numpy())),
+    "norm_mean_abs": ("rms_norm", lambda orig: (
+        lambda x, g, eps: np.asarray(x) / (np.mean(np.abs(x), axis=1, keepdims=True) + eps) * g)),
+    "norm_eps_outside_sqrt": ("rms_norm", lambda orig: (
+        lambda x, g, eps: np.asarray(x) / (np.sqrt(np.mean(np.asarray(x) ** 2, axis=1, keepdims=True)) + eps) * g)),
+    "block_no_residual": ("block_forward", lambda orig: (
+        lambda x, *a, **kw: (lambda o: (o[0] - (np.asarray(x, np.float64) if kw.get("tokens") is None
+                                               else np.asarray(x, np.float64)[kw["tokens"]]), o[1], o[2]))(
+            orig(x, *a, **kw)))),
 }
 
 
