@@ -7,7 +7,8 @@ Default workload: Kimi-K2 decode, T = 128 tokens, bf16, all 384 experts + 1
 shared resident.  For an expert-parallel rank workload (ep_size > 1) a step
 is that rank's expert FFN share (moe_expert_ffn over the rows dispatched to
 its local experts plus the shared expert over its own tokens), and value is
-the rank's own tokens per second.  Prints ONE JSON line (value = tokens/s) with:
+the rank's own tokens per second.  For a sub-block workload (block) a step is
+one moe_block_forward (pre-MoE RMSNorm, the layer, the residual add).  Prints ONE JSON line (value = tokens/s) with:
   roofline      -- the dominant kernel (grouped gate_up GEMM): algorithmic
                    bytes or flops per launch / its mean duration, timed with
                    HIP events the library records around that launch;
@@ -76,7 +77,8 @@ def kernel_hash() -> str:
 
 def setup(wl: gen.Workload, T: int):
     x = gen.gen_x(wl, T).cuda()
-    d = {"x": x, "router_w": gen.gen_router(wl).cuda(), "router_bias": gen.gen_bias(wl).cuda()}
+    d = {"x": x, "router_w": gen.gen_router(wl).cuda(), "router_bias": gen.gen_bias(wl).cuda(),
+         "norm_weight": gen.gen_norm_weight(wl).cuda()}
     d.update(gen.gen_expert_weights(wl, device="cuda"))
     torch.cuda.synchronize()
     return d
@@ -141,11 +143,14 @@ def cpu_baseline(wl, case, T, budget_s):
     kw = dict(num_experts_per_tok=wl.num_experts_per_tok, n_group=wl.n_group, topk_group=wl.topk_group,
               norm_topk_prob=wl.norm_topk_prob, routed_scaling_factor=wl.routed_scaling_factor)
     fp8 = wl.weight_dtype == gen.FP8
+    g64, eps = case["norm_weight"].double().cpu().numpy(), float(np.float32(wl.rms_norm_eps))
+    # what the router sees: x, or for the sub-block the rounded RMSNorm of x
+    xin = oracle.round_act(oracle.rms_norm(x64, g64, eps), wl.act_dtype) if wl.block else x64
     # one token first to size the sample to the time budget
     n = 1
     while True:
         toks = np.linspace(0, T - 1, n).astype(np.int64) if n > 1 else np.array([0])
-        need = np.unique(oracle.route(x64[toks], rw, b, **kw).ids)
+        need = np.unique(oracle.route(xin[toks], rw, b, **kw).ids)
         host = {}
         for e in need:  # host copies of the stored weights (outside the timed region)
             host[int(e)] = {m: case["w_" + m][e].cpu() for m in ("gate", "up", "down")}
@@ -160,10 +165,13 @@ def cpu_baseline(wl, case, T, budget_s):
                 return oracle.dequant_weight(d[m].numpy(), d["s_" + m].numpy())
             return d[m].to(torch.float64).numpy()
 
+        ex = lambda e: tuple(mat(host[e], m) for m in ("gate", "up", "down"))  # noqa: E731
+        shw = tuple(mat(sh, m) for m in ("gate", "up", "down")) if wl.n_shared_experts else None
         t0 = time.perf_counter()
-        oracle.layer_forward(x64, rw, b, lambda e: tuple(mat(host[e], m) for m in ("gate", "up", "down")),
-                             tuple(mat(sh, m) for m in ("gate", "up", "down")) if wl.n_shared_experts else None,
-                             fp8_act=fp8, tokens=toks, **kw)
+        if wl.block:
+            oracle.block_forward(x64, g64, eps, rw, b, ex, shw, act_dtype=wl.act_dtype, fp8_act=fp8, tokens=toks, **kw)
+        else:
+            oracle.layer_forward(x64, rw, b, ex, shw, fp8_act=fp8, tokens=toks, **kw)
         dt = time.perf_counter() - t0
         if dt >= budget_s / 3 or n >= T or n >= 64:
             break
@@ -210,8 +218,14 @@ def make_step(cfg, weights, wl, case, T):
     wts = torch.empty((T, wl.num_experts_per_tok), dtype=torch.float32, device="cuda")
     ws = B.alloc_workspace(cfg, T)
 
+    eps = float(np.float32(wl.rms_norm_eps))
+
     def step():
-        B.moe_layer_forward(cfg, weights, case["x"], case["router_w"], case["router_bias"], out, ws, ids, wts)
+        if wl.block:
+            B.moe_block_forward(cfg, weights, case["x"], case["norm_weight"], eps, case["router_w"],
+                                case["router_bias"], out, ws, ids, wts)
+        else:
+            B.moe_layer_forward(cfg, weights, case["x"], case["router_w"], case["router_bias"], out, ws, ids, wts)
     return step, ids
 
 
@@ -316,7 +330,7 @@ def main():
     detail = {}
     if args.breakdown:
         names = ["router_logits", "router_topk", "permute", "tiles", "gather", "act_quant", "gate_up", "down",
-                 "combine"]
+                 "combine", "norm"]
         per = {n: [] for n in names}
         for _ in range(5):
             pairs = [(hip.event(), hip.event()) for _ in names]

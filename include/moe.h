@@ -159,6 +159,23 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
                                void* out, int32_t* topk_ids_out, float* topk_weights_out,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* The MoE sub-block of a decoder layer: the pre-MoE RMSNorm, the layer, and
+ * the residual add ("Kimi K2 Base" architecture table: RMSNorm; raw config
+ * fields: rms_norm_eps 1e-06):
+ *   u[t]   = act( x[t] / sqrt(mean_h x[t][h]^2 + rms_norm_eps) * norm_weight ),
+ *            computed in fp64 and rounded once to act_dtype (nearest even);
+ *   out[t] = act( x[t] + shared(u[t]) + sum_j w_tj expert_j(u[t]) ),
+ *            accumulated in fp32 in that order, rounded once.
+ * Routing and the experts see u exactly as moe_layer_forward sees its x (with
+ * fp8 weights the same pass writes u's e4m3 codes).  x [T][H] act_dtype is
+ * the residual stream; norm_weight [H] act_dtype; rms_norm_eps in [0, 1).
+ * Other arguments as moe_layer_forward; out may not alias x. */
+moe_status_t moe_block_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                               const void* norm_weight, float rms_norm_eps, const void* router_w,
+                               const float* router_bias, int64_t num_tokens, void* out,
+                               int32_t* topk_ids_out, float* topk_weights_out, void* ws,
+                               size_t ws_bytes, void* stream);
+
 const char* moe_status_string(moe_status_t status);
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* moe_last_error(void);
@@ -178,7 +195,8 @@ enum {
   MOE_KID_GATE_UP = 6,       /* grouped gate/up GEMM + SiLU * up               */
   MOE_KID_DOWN = 7,          /* grouped down GEMM                              */
   MOE_KID_COMBINE = 8,       /* weighted combine + shared add                  */
-  MOE_KID_COUNT = 9
+  MOE_KID_NORM = 9,          /* pre-MoE RMSNorm (moe_block_forward)            */
+  MOE_KID_COUNT = 10
 };
 moe_status_t moe_profile_arm(int32_t kernel_id, void* ev_start, void* ev_stop);
 

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 (MOE_KID_ROUTER_LOGITS, MOE_KID_ROUTER_TOPK, MOE_KID_PERMUTE, MOE_KID_TILES, MOE_KID_GATHER,
- MOE_KID_ACT_QUANT, MOE_KID_GATE_UP, MOE_KID_DOWN, MOE_KID_COMBINE, MOE_KID_COUNT) = range(10)
+ MOE_KID_ACT_QUANT, MOE_KID_GATE_UP, MOE_KID_DOWN, MOE_KID_COMBINE, MOE_KID_NORM, MOE_KID_COUNT) = range(11)
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
 
@@ -96,6 +96,7 @@ def load() -> ctypes.CDLL:
         "moe_expert_ffn": (st, [CP, WP, _P, _P, _P, _P, i64, _P, _P, _P, sz, _P]),
         "moe_combine": (st, [CP, _P, _P, _P, _P, i64, _P, _P]),
         "moe_layer_forward": (st, [CP, WP, _P, _P, _P, i64, _P, _P, _P, _P, sz, _P]),
+        "moe_block_forward": (st, [CP, WP, _P, _P, ctypes.c_float, _P, _P, i64, _P, _P, _P, _P, sz, _P]),
         "moe_status_string": (ctypes.c_char_p, [st]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (ctypes.c_int, []),
@@ -175,6 +176,14 @@ def moe_layer_forward(cfg, weights: MoeWeights, x, router_w, router_bias, out, w
                                     _ptr(router_bias), x.shape[0], _ptr(out), _ptr(topk_ids),
                                     _ptr(topk_weights), _ptr(ws), _nbytes(ws), _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_block_forward(cfg, weights: MoeWeights, x, norm_weight, rms_norm_eps, router_w, router_bias, out, ws,
+                      topk_ids=None, topk_weights=None, stream=None):
+    _check(load().moe_block_forward(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x), _ptr(norm_weight),
+                                    float(rms_norm_eps), _ptr(router_w), _ptr(router_bias), x.shape[0], _ptr(out),
+                                    _ptr(topk_ids), _ptr(topk_weights), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_block_forward")
 
 
 def moe_profile_arm(kernel_id: int, ev_start: Optional[int] = None, ev_stop: Optional[int] = None):

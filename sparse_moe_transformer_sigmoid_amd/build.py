@@ -17,7 +17,7 @@ OUT = os.path.join(PKG, "libmoe.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["abi.hip", "router.hip", "permute.hip", "ffn_stream.hip", "ffn_fp8.hip", "ffn_tile.hip", "ffn_tile_fp8.hip", "combine.hip"]
+SOURCES = ["abi.hip", "router.hip", "permute.hip", "ffn_stream.hip", "ffn_fp8.hip", "ffn_tile.hip", "ffn_tile_fp8.hip", "combine.hip", "norm.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-munsafe-fp-atomics", "-I", os.path.join(PKG, "..", "include")]

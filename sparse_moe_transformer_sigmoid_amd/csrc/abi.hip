@@ -118,7 +118,7 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0
 // --------------------------------------------------------------------------
 struct Layout {
   size_t logits, ids, w, ccount, cbase, offsets, rows, inv, tiles, tcount, xq, xs, h, hq, hs, hsh,
-      hqsh, hssh, y, ysh, total;
+      hqsh, hssh, y, ysh, u, total;
 };
 
 Layout layout(const moe_config_t* c, int64_t T) {
@@ -155,6 +155,7 @@ Layout layout(const moe_config_t* c, int64_t T) {
   L.hssh = take(fp8(c) ? T * (Fs / 128) * 4 : 0);
   L.y = take(T * k * H * asz);
   L.ysh = take(T * H * asz);
+  L.u = take(T * H * asz);
   L.total = off;
   return L;
 }
@@ -309,6 +310,61 @@ FfnArgs ffn_args(const moe_config_t* c, int64_t T, void* ws) {
   return f;
 }
 
+moe_status_t check_layer_args(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                              const void* router_w, const float* router_bias, int64_t T, void* out,
+                              int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes) {
+  TRY(check_cfg(cfg));
+  TRY(check_T(T));
+  if (T == 0) return MOE_OK;
+  TRY(check_weights(cfg, w));
+  NEED(x);
+  NEED(router_w);
+  NEED(router_bias);
+  NEED(out);
+  if (topk_ids_out && !aligned(topk_ids_out)) return fail(MOE_ERR_INVALID_ARG, "topk_ids_out is not 16-byte aligned");
+  if (topk_weights_out && !aligned(topk_weights_out)) return fail(MOE_ERR_INVALID_ARG, "topk_weights_out is not 16-byte aligned");
+  return check_ws(cfg, T, ws, ws_bytes);
+}
+
+// route -> group -> expert FFNs -> combine on layer input x; `resid` (nullable)
+// is added in the combine; `x_quantised`: the fp8 codes of x are already in
+// the workspace
+moe_status_t run_layer(const moe_config_t* cfg, const moe_weights_t* w, const void* x, const void* router_w,
+                       const float* router_bias, int64_t T, void* out, int32_t* topk_ids_out,
+                       float* topk_weights_out, void* ws, hipStream_t st, const void* resid,
+                       bool x_quantised) {
+  const Layout L = layout(cfg, T);
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+  float* wts = topk_weights_out ? topk_weights_out : at<float>(ws, L.w);
+  TRY(run_route(cfg, x, router_w, router_bias, T, ids, wts, ws, st));
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* rows = at<int32_t>(ws, L.rows);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  TRY(run_permute(cfg, ids, T, offsets, rows, inv, true, ws, st));
+  FfnArgs f = ffn_args(cfg, T, ws);
+  f.offsets = offsets;
+  f.xr = x;
+  f.xr_rows = rows;
+  f.xs = x;
+  f.y = at<void>(ws, L.y);
+  f.y_sh = at<void>(ws, L.ysh);
+  if (fp8(cfg)) {
+    uint8_t* xq = at<uint8_t>(ws, L.xq);
+    float* xs = at<float>(ws, L.xs);
+    if (!x_quantised)
+      MOE_LAUNCH(MOE_KID_ACT_QUANT, launch_act_quant(static_cast<const uint16_t*>(x), T, cfg->hidden_size, xq, xs, st));
+    f.xr = xq;
+    f.xr_scales = xs;
+    f.xs = xq;
+    f.xs_scales = xs;
+  }
+  TRY(run_ffn(cfg, w, f, T, ws, st));
+  CombineArgs a{f.y, cfg->n_shared_experts > 0 ? f.y_sh : nullptr, wts, inv, static_cast<int>(T),
+                cfg->num_experts_per_tok, cfg->hidden_size, out, resid};
+  MOE_LAUNCH(MOE_KID_COMBINE, launch_combine(a, cfg->act_dtype == MOE_BF16, st));
+  return MOE_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -458,48 +514,34 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
                                int32_t* topk_ids_out, float* topk_weights_out, void* ws,
                                size_t ws_bytes, void* stream) {
   g_err.clear();
-  TRY(check_cfg(cfg));
-  TRY(check_T(T));
+  TRY(check_layer_args(cfg, w, x, router_w, router_bias, T, out, topk_ids_out, topk_weights_out, ws, ws_bytes));
   if (T == 0) return MOE_OK;
-  TRY(check_weights(cfg, w));
-  NEED(x);
-  NEED(router_w);
-  NEED(router_bias);
-  NEED(out);
-  if (topk_ids_out && !aligned(topk_ids_out)) return fail(MOE_ERR_INVALID_ARG, "topk_ids_out is not 16-byte aligned");
-  if (topk_weights_out && !aligned(topk_weights_out)) return fail(MOE_ERR_INVALID_ARG, "topk_weights_out is not 16-byte aligned");
-  TRY(check_ws(cfg, T, ws, ws_bytes));
+  (void)hipGetLastError();
+  return run_layer(cfg, w, x, router_w, router_bias, T, out, topk_ids_out, topk_weights_out, ws,
+                   static_cast<hipStream_t>(stream), nullptr, false);
+}
+
+moe_status_t moe_block_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                               const void* norm_weight, float rms_norm_eps, const void* router_w,
+                               const float* router_bias, int64_t T, void* out, int32_t* topk_ids_out,
+                               float* topk_weights_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err.clear();
+  TRY(check_layer_args(cfg, w, x, router_w, router_bias, T, out, topk_ids_out, topk_weights_out, ws, ws_bytes));
+  if (T == 0) return MOE_OK;
+  NEED(norm_weight);
+  if (!(rms_norm_eps >= 0.0f) || !(rms_norm_eps < 1.0f))
+    return fail(MOE_ERR_INVALID_ARG, "rms_norm_eps %g not in [0, 1)", static_cast<double>(rms_norm_eps));
   (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Layout L = layout(cfg, T);
-  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
-  float* wts = topk_weights_out ? topk_weights_out : at<float>(ws, L.w);
-  TRY(run_route(cfg, x, router_w, router_bias, T, ids, wts, ws, st));
-  int32_t* offsets = at<int32_t>(ws, L.offsets);
-  int32_t* rows = at<int32_t>(ws, L.rows);
-  int32_t* inv = at<int32_t>(ws, L.inv);
-  TRY(run_permute(cfg, ids, T, offsets, rows, inv, true, ws, st));
-  FfnArgs f = ffn_args(cfg, T, ws);
-  f.offsets = offsets;
-  f.xr = x;
-  f.xr_rows = rows;
-  f.xs = x;
-  f.y = at<void>(ws, L.y);
-  f.y_sh = at<void>(ws, L.ysh);
-  if (fp8(cfg)) {
-    uint8_t* xq = at<uint8_t>(ws, L.xq);
-    float* xs = at<float>(ws, L.xs);
-    MOE_LAUNCH(MOE_KID_ACT_QUANT, launch_act_quant(static_cast<const uint16_t*>(x), T, cfg->hidden_size, xq, xs, st));
-    f.xr = xq;
-    f.xr_scales = xs;
-    f.xs = xq;
-    f.xs_scales = xs;
-  }
-  TRY(run_ffn(cfg, w, f, T, ws, st));
-  CombineArgs a{f.y, cfg->n_shared_experts > 0 ? f.y_sh : nullptr, wts, inv, static_cast<int>(T),
-                cfg->num_experts_per_tok, cfg->hidden_size, out};
-  MOE_LAUNCH(MOE_KID_COMBINE, launch_combine(a, cfg->act_dtype == MOE_BF16, st));
-  return MOE_OK;
+  void* u = at<void>(ws, L.u);
+  // fp8 weights: the norm pass also writes the e4m3 codes of u
+  uint8_t* codes = fp8(cfg) ? at<uint8_t>(ws, L.xq) : nullptr;
+  float* scales = fp8(cfg) ? at<float>(ws, L.xs) : nullptr;
+  MOE_LAUNCH(MOE_KID_NORM, launch_rmsnorm(x, norm_weight, static_cast<double>(rms_norm_eps), T, cfg->hidden_size,
+                                          cfg->act_dtype == MOE_BF16, u, codes, scales, st));
+  return run_layer(cfg, w, u, router_w, router_bias, T, out, topk_ids_out, topk_weights_out, ws, st, x,
+                   fp8(cfg));
 }
 
 }  // extern "C"

@@ -2,7 +2,9 @@
 //   out[t] = y_shared[t] + sum_j w[t][j] * y[inv[t*k + j]]
 // (norm_topk_prob / routed_scaling_factor are already in w; the shared expert
 // has weight 1 -- "Kimi K2 Base" raw config fields: n_shared_experts 1).
-// fp32 accumulation in slot order, one rounding at the end; one block per
+// With a residual (the sub-block around the layer) the sum starts from it:
+//   out[t] = resid[t] + y_shared[t] + sum_j w[t][j] * y[inv[t*k + j]].
+// fp32 accumulation in that order, one rounding at the end; one block per
 // token, 16-byte vectors.
 #include "kernels.h"
 
@@ -25,17 +27,26 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
     if (BF16) {
       const uint16_t* ysh = static_cast<const uint16_t*>(a.y_sh);
       const uint16_t* y = static_cast<const uint16_t*>(a.y);
-      if (ysh) {
-        uint4 v = reinterpret_cast<const uint4*>(ysh + t * a.H)[c];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+      const uint16_t* res = static_cast<const uint16_t*>(a.resid);
+      if (res) {
+        uint4 v = reinterpret_cast<const uint4*>(res + t * a.H)[c];
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc[2 * i] = bf16_to_f32(static_cast<uint16_t>(w4[i] & 0xffffu));
           acc[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w4[i] >> 16));
         }
-      } else {
+      }
+      if (ysh) {
+        uint4 v = reinterpret_cast<const uint4*>(ysh + t * a.H)[c];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(w4[i] & 0xffffu));
+          acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(w4[i] >> 16));
+        }
       }
       for (int j = 0; j < a.k; ++j) {
         uint4 v = reinterpret_cast<const uint4*>(y + rs[j] * a.H)[c];
@@ -57,8 +68,13 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
     } else {
       const float* ysh = static_cast<const float*>(a.y_sh);
       const float* y = static_cast<const float*>(a.y);
-      float4 s = ysh ? reinterpret_cast<const float4*>(ysh + t * a.H)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      acc[0] = s.x; acc[1] = s.y; acc[2] = s.z; acc[3] = s.w;
+      const float* res = static_cast<const float*>(a.resid);
+      float4 r = res ? reinterpret_cast<const float4*>(res + t * a.H)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      acc[0] = r.x; acc[1] = r.y; acc[2] = r.z; acc[3] = r.w;
+      if (ysh) {
+        float4 s = reinterpret_cast<const float4*>(ysh + t * a.H)[c];
+        acc[0] += s.x; acc[1] += s.y; acc[2] += s.z; acc[3] += s.w;
+      }
       for (int j = 0; j < a.k; ++j) {
         float4 v = reinterpret_cast<const float4*>(y + rs[j] * a.H)[c];
         const float wj = ws[j];

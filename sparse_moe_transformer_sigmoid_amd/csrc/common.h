@@ -70,6 +70,15 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Dynamic activation quantisation of one 128-channel group held by a wave as
+// two values per lane: s = amax / 448 (1 for an all-zero group), codes
+// e4m3(v / s), the division in fp32.  Returns the lane's two codes.
+__device__ __forceinline__ uint16_t quant_pair(float v0, float v1, float& s) {
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  s = amax > 0.f ? amax / 448.0f : 1.0f;
+  return static_cast<uint16_t>(f32_to_e4m3(v0 / s)) | (static_cast<uint16_t>(f32_to_e4m3(v1 / s)) << 8);
+}
+
 // ---- grouped-GEMM work list ----------------------------------------------
 // One entry per (group, tile of up to BM grouped rows).  Groups 0..E-1 are the
 // routed experts (rows [offsets[e], offsets[e+1]) of the grouped order), group

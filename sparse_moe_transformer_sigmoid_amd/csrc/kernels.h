@@ -105,6 +105,12 @@ hipError_t launch_gate_up_tile(const FfnArgs& a, hipStream_t st);  // ffn_tile.h
 hipError_t launch_down_tile(const FfnArgs& a, hipStream_t st);
 int tile_rows();
 
+// pre-MoE RMSNorm, fp64, rounded once to the activation dtype into u [T][H];
+// with `codes` (bf16 only) also the fp8 quantisation of u (codes [T][H],
+// scales [T][H/128]); H a multiple of 128
+hipError_t launch_rmsnorm(const void* x, const void* g, double eps, int64_t T, int H, bool bf16, void* u,
+                          uint8_t* codes, float* scales, hipStream_t st);
+
 struct CombineArgs {
   const void* y;
   const void* y_sh;
@@ -112,6 +118,7 @@ struct CombineArgs {
   const int32_t* inv;
   int T, k, H;
   void* out;
+  const void* resid;   // nullable: residual stream added first (act dtype)
 };
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t st);
 

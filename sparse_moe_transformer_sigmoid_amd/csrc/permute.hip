@@ -218,12 +218,9 @@ __global__ __launch_bounds__(256) void act_quant_rows(const In* __restrict__ src
   if (gi >= R * groups) return;
   const int64_t row = gi / groups;
   const int g = static_cast<int>(gi - row * groups);
-  float v0, v1;
+  float v0, v1, s;
   load_pair(src + row * C + g * 128 + 2 * lane, v0, v1);
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-  const uint16_t c = static_cast<uint16_t>(f32_to_e4m3(v0 / s)) |
-                     (static_cast<uint16_t>(f32_to_e4m3(v1 / s)) << 8);
+  const uint16_t c = quant_pair(v0, v1, s);
   *reinterpret_cast<uint16_t*>(codes + row * C + g * 128 + 2 * lane) = c;
   if (lane == 0) scales[row * groups + g] = s;
 }

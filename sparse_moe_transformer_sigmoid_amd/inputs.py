@@ -86,6 +86,9 @@ class Workload:
     # (which its shared expert serves) and the routed rows arrive dispatched
     # from a global batch of num_tokens * ep_size tokens
     ep_size: int = 1
+    # True: the workload is the sub-block around the layer (pre-MoE RMSNorm,
+    # the layer, the residual add); x is then the residual stream
+    block: bool = False
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -130,6 +133,8 @@ WORKLOADS: Dict[str, Workload] = {
     "moonlight_bf16": Workload("moonlight_bf16", 256, 2048, 1408, 64, 6, n_shared_experts=2),
     # the dense first layer (first_k_dense_replace 1, intermediate_size 18432)
     # as one always-selected expert of weight 1: E = 1, k = 1, no shared
+    # the same decode batch through the sub-block (RMSNorm + layer + residual)
+    "k2_block_decode_bf16": _k2("k2_block_decode_bf16", 128, block=True),
     "k2_dense_layer_bf16": _k2("k2_dense_layer_bf16", 128, moe_intermediate_size=18432, n_routed_experts=1,
                                num_experts_per_tok=1, n_shared_experts=0, routed_scaling_factor=1.0,
                                bias="zero"),

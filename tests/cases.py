@@ -25,7 +25,9 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def bad_rows(wl, x64, router64, bias64):
+def bad_rows(wl, x64, router64, bias64, rows=None, transform=None):
+    if transform is not None:
+        x64 = transform(x64, rows)
     r = oracle.route(x64, router64, bias64, **route_kwargs(wl))
     gap = oracle.selection_gap(r, wl.num_experts_per_tok)
     ggap = oracle.group_gap(r, wl.n_group, wl.topk_group)
@@ -33,13 +35,14 @@ def bad_rows(wl, x64, router64, bias64):
 
 
 def enforce_gap(wl: gen.Workload, x: torch.Tensor, router_w: torch.Tensor, bias: torch.Tensor,
-                max_passes: int = 40) -> torch.Tensor:
-    """Redraw token rows of x (CPU tensor) until every token's gap >= MIN_GAP."""
+                max_passes: int = 40, transform=None) -> torch.Tensor:
+    """Redraw token rows of x (CPU tensor) until every token's gap >= MIN_GAP.
+    `transform(x64, rows)` maps rows of x to what the router sees."""
     x = x.clone()
     r64, b64 = to64(router_w), to64(bias)
     rows = np.arange(x.shape[0])
     for attempt in range(max_passes):
-        bad = rows[bad_rows(wl, to64(x[rows]), r64, b64)]
+        bad = rows[bad_rows(wl, to64(x[rows]), r64, b64, rows, transform)]
         if len(bad) == 0:
             return x
         x[bad] = gen.gen_x_rows(wl, bad, attempt)
@@ -119,3 +122,44 @@ def oracle_rank_share(wl: gen.Workload, case: dict):
     sh = shared_weights(wl, case)
     y_sh = oracle.swiglu_expert(to64(case["x"]), *sh) if sh is not None else None
     return y, y_sh
+
+
+# ------------------------------------------- the sub-block around the layer --
+def eps32(wl: gen.Workload) -> float:
+    """rms_norm_eps as the fp32 value the C ABI receives."""
+    return float(np.float32(wl.rms_norm_eps))
+
+
+def row_scales(T: int) -> np.ndarray:
+    """Per-token powers of two (exact in bf16/fp32) so that rows of the
+    residual stream differ in magnitude: 2^(t % 5 - 2)."""
+    return np.ldexp(1.0, (np.arange(T) % 5) - 2)
+
+
+def make_block_case(wl: gen.Workload, device="cpu", num_tokens=None) -> dict:
+    """Inputs of the sub-block: residual stream x (rows scaled by row_scales),
+    RMSNorm weight, router and experts; the routing gap is enforced on what the
+    router sees, the activation-dtype rounding of rms_norm(x)."""
+    x = gen.gen_x(wl, num_tokens)
+    T = x.shape[0]
+    g, rw, b = gen.gen_norm_weight(wl), gen.gen_router(wl), gen.gen_bias(wl)
+    sc = row_scales(T)
+    g64, eps = to64(g), eps32(wl)
+
+    def to_u(x64, rows):
+        return oracle.round_act(oracle.rms_norm(x64 * sc[rows, None], g64, eps), wl.act_dtype)
+
+    if T > 0:
+        x = enforce_gap(wl, x, rw, b, transform=to_u)
+    x = x * torch.from_numpy(sc).to(x.dtype)[:, None]
+    d = {"x": x.to(device), "norm_weight": g.to(device), "router_w": rw.to(device), "router_bias": b.to(device)}
+    d.update(gen.gen_expert_weights(wl, device))
+    return d
+
+
+def oracle_block(wl: gen.Workload, case: dict, tokens=None):
+    """fp64 oracle of the sub-block: (out, Route, u)."""
+    return oracle.block_forward(
+        to64(case["x"]), to64(case["norm_weight"]), eps32(wl), to64(case["router_w"]),
+        to64(case["router_bias"]), expert_fn(wl, case), shared_weights(wl, case), act_dtype=wl.act_dtype,
+        fp8_act=(wl.weight_dtype == gen.FP8), tokens=tokens, **route_kwargs(wl))

@@ -96,3 +96,30 @@ def check_route(ids: torch.Tensor, w: torch.Tensor, route, rows=None):
     assert len(bad) == 0, f"routing differs on {len(bad)} tokens, first {bad[:5]}"
     rel = np.abs(w_np - route.weights) / np.abs(route.weights)
     assert rel.max() <= W_RTOL, f"routing weights rel err {rel.max():.3g}"
+
+
+def run_block(wl: gen.Workload, case: dict):
+    """moe_block_forward on `case`; returns out, ids, weights."""
+    cfg = cfg_of(wl)
+    x = case["x"]
+    T, k = x.shape[0], wl.num_experts_per_tok
+    out = torch.empty((T, wl.hidden_size), dtype=act_dtype(wl), device=x.device)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    ws = B.alloc_workspace(cfg, T)
+    B.moe_block_forward(cfg, B.MoeWeights.from_tensors(case), x, case["norm_weight"], float(np.float32(wl.rms_norm_eps)),
+                        case["router_w"], case["router_bias"], out, ws, ids, w)
+    torch.cuda.synchronize()
+    return out, ids, w
+
+
+def block_err(got: torch.Tensor, ref: np.ndarray, x: np.ndarray, act: str) -> float:
+    """Error of a sub-block output in units of max|layer part|, after allowing
+    one unit in the last place of the output's rounding (bf16: 2^-8 |ref|,
+    fp32: 2^-22 |ref|): the layer part ref - x carries the layer tolerance,
+    the residual only the final rounding."""
+    g = got.detach().to("cpu", torch.float64).numpy()
+    ulp = 2.0 ** -8 if act == gen.BF16 else 2.0 ** -22
+    excess = np.maximum(np.abs(g - ref) - ulp * np.abs(ref), 0.0)
+    scale = np.abs(ref - x).max()
+    return float(excess.max() / scale)

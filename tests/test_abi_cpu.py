@@ -173,3 +173,20 @@ def test_dispatch_counts_follow_the_global_batch():
     assert c.shape == (48,)
     assert abs(c.mean() - 128 * 8 * 8 / 384) < 3
     assert (gen.gen_dispatch_counts(wl) == c).all()
+
+
+def test_block_forward_validates_norm_arguments():
+    c = k2cfg()
+    lib = B.load()
+    w = B.MoeWeights()
+    for n in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
+        setattr(w, n, FAKE)
+    st = lib.moe_block_forward(ctypes.byref(c), ctypes.byref(w), FAKE, None, ctypes.c_float(1e-6), FAKE, FAKE, 4,
+                               FAKE, None, None, FAKE * 16, 1 << 40, None)
+    assert st == B.MOE_ERR_INVALID_ARG and "norm_weight" in B.moe_last_error()
+    st = lib.moe_block_forward(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, ctypes.c_float(-1.0), FAKE, FAKE, 4,
+                               FAKE, None, None, FAKE * 16, 1 << 40, None)
+    assert st == B.MOE_ERR_INVALID_ARG and "rms_norm_eps" in B.moe_last_error()
+    st = lib.moe_block_forward(ctypes.byref(c), ctypes.byref(w), None, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, 0,
+                               None, None, None, None, 0, None)
+    assert st == B.MOE_OK  # T = 0: nothing touched

@@ -12,7 +12,7 @@ import torch
 
 import cases
 import oracle
-from gpu_util import TOL, check_route, rel_err, run_layer, run_stages, say
+from gpu_util import TOL, block_err, check_route, rel_err, run_block, run_layer, run_stages, say
 from sparse_moe_transformer_sigmoid_amd import binding as B
 from sparse_moe_transformer_sigmoid_amd import inputs as gen
 
@@ -273,3 +273,74 @@ def test_ep_rank_share_full_size(name):
     err, err_sh = rel_err(y[:R], ref), rel_err(y_sh, ref_sh)
     say(f"  rel err routed {err:.3e} shared {err_sh:.3e}")
     assert err <= TOL[wl.weight_dtype] and err_sh <= TOL[wl.weight_dtype]
+
+
+# ------------------------------------------- the sub-block around the layer --
+BLOCK = [
+    (W["tiny_fp32"], 16), (W["small_bf16"], 1), (W["small_bf16"], 40), (W["small_bf16"], 300),
+    (W["small_bf16"], 1024), (W["small_grouped_bf16"], 100), (W["small_fp8"], 100), (W["small_fp8"], 300),
+]
+
+
+@pytest.mark.parametrize("wl,T", BLOCK, ids=[f"{w.name}-T{t}" for w, t in BLOCK])
+def test_block_matches_oracle_small(wl, T):
+    """moe_block_forward = RMSNorm (fp64, one rounding) -> layer -> residual
+    add, against the oracle's block_forward on every row."""
+    say(f"[case] block {wl.name} T={T}")
+    case = cases.make_block_case(wl, device="cuda", num_tokens=T)
+    out, ids, w = run_block(wl, case)
+    ref, route, _ = cases.oracle_block(wl, case)
+    check_route(ids, w, route)
+    err = block_err(out, ref, cases.to64(case["x"]), wl.act_dtype)
+    say(f"  err {err:.3e} of max|layer part| (tol {TOL[wl.weight_dtype]})")
+    assert err <= TOL[wl.weight_dtype]
+
+
+def test_block_with_zero_experts_is_the_residual():
+    """All expert weights zero: the output is the residual stream, bit for bit."""
+    wl = W["small_bf16"]
+    case = cases.make_block_case(wl, device="cuda", num_tokens=50)
+    for k in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
+        case[k] = torch.zeros_like(case[k])
+    out, _, _ = run_block(wl, case)
+    assert torch.equal(out, case["x"])
+
+
+def full_block_case(wl, weights, T):
+    say(f"[case] block {wl.name} T={T}")
+    x = gen.gen_x(wl, T)
+    g, rw, b = gen.gen_norm_weight(wl), gen.gen_router(wl), gen.gen_bias(wl)
+    sc = cases.row_scales(T)
+    g64, eps = cases.to64(g), cases.eps32(wl)
+    x = cases.enforce_gap(wl, x, rw, b, transform=lambda x64, rows: oracle.round_act(
+        oracle.rms_norm(x64 * sc[rows, None], g64, eps), wl.act_dtype))
+    x = x * torch.from_numpy(sc).to(x.dtype)[:, None]
+    d = {"x": x.cuda(), "norm_weight": g.cuda(), "router_w": rw.cuda(), "router_bias": b.cuda()}
+    d.update(weights)
+    return d
+
+
+@pytest.mark.parametrize("T", [128, 8])
+def test_k2_block_decode_full_size(k2_weights, T):
+    wl = W["k2_decode_bf16"]
+    case = full_block_case(wl, k2_weights, T)
+    out, ids, w = run_block(wl, case)
+    tokens = np.array([0, T - 1])
+    ref, route, _ = cases.oracle_block(wl, case, tokens=tokens)
+    check_route(ids, w, route, rows=tokens)
+    err = block_err(out[torch.as_tensor(tokens, device="cuda")], ref, cases.to64(case["x"])[tokens], wl.act_dtype)
+    say(f"  sampled tokens {list(tokens)}: err {err:.3e}")
+    assert err <= TOL[wl.weight_dtype]
+
+
+def test_k2_block_fp8_full_size(k2_fp8_weights):
+    wl = W["k2_fp8"]
+    T = 64
+    case = full_block_case(wl, k2_fp8_weights, T)
+    out, ids, w = run_block(wl, case)
+    tokens = np.array([0, T - 1])
+    ref, route, _ = cases.oracle_block(wl, case, tokens=tokens)
+    check_route(ids, w, route, rows=tokens)
+    err = block_err(out[torch.as_tensor(tokens, device="cuda")], ref, cases.to64(case["x"])[tokens], wl.act_dtype)
+    say(f"  sampled tokens {list(tokens)}: err {err:.3e}")
+    assert err <= TOL[wl.weight_dtype]
