@@ -135,7 +135,7 @@ Layout layout(const moe_config_t* c, int64_t T) {
     off += (bytes + 255) & ~size_t(255);
     return o;
   };
-  L.logits = take(T * E * 4);
+  L.logits = take(router_kparts(T, static_cast<int>(E), static_cast<int>(H), c->act_dtype == MOE_BF16) * T * E * 4);
   L.ids = take(T * k * 4);
   L.w = take(T * k * 4);
   L.ccount = take(nchunk * E * 4);

@@ -21,8 +21,10 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
   }
   __syncthreads();
   constexpr int VEC = BF16 ? 8 : 4;
-  const int nv = a.H / VEC;
-  for (int c = threadIdx.x; c < nv; c += blockDim.x) {
+  // columns split over gridDim.y blocks per token (few tokens: more blocks)
+  const int nv = a.H / VEC, per = (nv + gridDim.y - 1) / gridDim.y;
+  const int c1 = min(nv, static_cast<int>(blockIdx.y + 1) * per);
+  for (int c = blockIdx.y * per + threadIdx.x; c < c1; c += blockDim.x) {
     float acc[VEC];
     if (BF16) {
       const uint16_t* ysh = static_cast<const uint16_t*>(a.y_sh);
@@ -89,8 +91,12 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t st) {
   const int threads = 256;
-  if (bf16) hipLaunchKernelGGL(combine_rows<true>, dim3(a.T), dim3(threads), 0, st, a);
-  else hipLaunchKernelGGL(combine_rows<false>, dim3(a.T), dim3(threads), 0, st, a);
+  // below 256 tokens, one block per token and 256 vectors of columns
+  const int nv = a.H / (bf16 ? 8 : 4);
+  const int split = a.T < 256 ? (nv + threads - 1) / threads : 1;
+  const dim3 grid(a.T, split);
+  if (bf16) hipLaunchKernelGGL(combine_rows<true>, grid, dim3(threads), 0, st, a);
+  else hipLaunchKernelGGL(combine_rows<false>, grid, dim3(threads), 0, st, a);
   return hipGetLastError();
 }
 

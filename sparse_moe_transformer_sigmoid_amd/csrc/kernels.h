@@ -18,6 +18,8 @@ struct RouterArgs {
   float* w;       // [T][k]
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t st);
+// K parts of the router logits (partial sums [kparts][T][E] in the logits scratch)
+int router_kparts(int64_t T, int E, int H, bool bf16);
 hipError_t launch_topk(const RouterArgs& a, hipStream_t st);
 
 struct PermArgs {

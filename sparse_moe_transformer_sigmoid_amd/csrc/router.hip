@@ -27,8 +27,12 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const uint16_t* __rest
   const uint16_t* pa = wr + static_cast<int64_t>(min(e0 + r, E - 1)) * H + q * 32;
   const uint16_t* pb = x + static_cast<int64_t>(tok) * H + q * 32;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int steps = H / 128;
-  for (int s = wave; s < steps; s += 4) {
+  // K part blockIdx.z of gridDim.z: steps [s0, s1) of 128; its partial sums
+  // go to logits + part * T * E
+  const int steps = H / 128, per = (steps + gridDim.z - 1) / gridDim.z;
+  const int s0 = blockIdx.z * per, s1 = min(s0 + per, steps);
+  logits += static_cast<int64_t>(blockIdx.z) * T * E;
+  for (int s = s0 + wave; s < s1; s += 4) {
     const uint4* a4 = reinterpret_cast<const uint4*>(pa + s * 128);
     const uint4* b4 = reinterpret_cast<const uint4*>(pb + s * 128);
     uint4 a[4], b[4];
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 // remaining eligible sel values (ties: lower expert id) by butterfly shuffles.
 // ---------------------------------------------------------------------------
 template <int V>
-__global__ __launch_bounds__(256) void router_topk(const float* __restrict__ logits,
+__global__ __launch_bounds__(256) void router_topk(const float* __restrict__ logits, int kparts,
                                                    const float* __restrict__ bias, int T, int E,
                                                    int k, int n_group, int topk_group, int norm,
                                                    float scale, int32_t* __restrict__ ids_out,
@@ -164,7 +168,9 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
   for (int i = 0; i < V; ++i) {
     const int e = lane * V + i;
     if (e < E) {
-      const float z = logits[static_cast<int64_t>(tt) * E + e];
+      // partial logits of the K parts, added in part order
+      float z = logits[static_cast<int64_t>(tt) * E + e];
+      for (int p = 1; p < kparts; ++p) z += logits[(static_cast<int64_t>(p) * T + tt) * E + e];
       s[i] = 1.0f / (1.0f + expf(-z));
       sel[i] = s[i] + bias[e];
     } else {
@@ -244,6 +250,17 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
   }
 }
 
+// K parts of the 16x16 logits kernel: few tokens give few blocks (24 for one
+// token and 384 experts), so the K loop is split over up to 8 blocks per tile
+// until the grid has ~512 blocks; the top-k kernel adds the parts in order
+int router_kparts(int64_t T, int E, int H, bool bf16) {
+  if (!bf16 || (T >= 512 && E % 64 == 0)) return 1;
+  const int64_t blocks = static_cast<int64_t>((E + 15) / 16) * ((T + 15) / 16);
+  int kp = 1;
+  while (kp < 8 && blocks * kp < 512 && (H / 128) >= 2 * kp * 4) kp *= 2;
+  return kp;
+}
+
 hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
   if (a.bf16 && a.T >= 512 && a.E % 64 == 0) {
     dim3 grid((a.T + 127) / 128, a.E / 64);
@@ -251,7 +268,7 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wr), a.T,
                        a.E, a.H, a.logits);
   } else if (a.bf16) {
-    dim3 grid((a.E + 15) / 16, (a.T + 15) / 16);
+    dim3 grid((a.E + 15) / 16, (a.T + 15) / 16, router_kparts(a.T, a.E, a.H, a.bf16));
     hipLaunchKernelGGL(router_logits_bf16, grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wr), a.T,
                        a.E, a.H, a.logits);
@@ -270,7 +287,8 @@ hipError_t launch_topk(const RouterArgs& a, hipStream_t st) {
   dim3 grid((a.T + 3) / 4), block(256);
   const int V = (a.E + 63) / 64;
 #define MOE_TOPK(VV)                                                                         \
-  hipLaunchKernelGGL(router_topk<VV>, grid, block, 0, st, a.logits, a.bias, a.T, a.E, a.k, \
+  hipLaunchKernelGGL(router_topk<VV>, grid, block, 0, st, a.logits, router_kparts(a.T, a.E, a.H, a.bf16), \
+                     a.bias, a.T, a.E, a.k,                                                   \
                      a.n_group, a.topk_group, a.norm, a.scale, a.ids, a.w)
   if (V <= 1) MOE_TOPK(1);
   else if (V <= 2) MOE_TOPK(2);
