@@ -118,8 +118,10 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0
 // --------------------------------------------------------------------------
 struct Layout {
   size_t logits, ids, w, ccount, cbase, offsets, rows, inv, tiles, tcount, xq, xs, h, hq, hs, hsh,
-      hqsh, hssh, y, ysh, u, total;
+      hqsh, hssh, y, ysh, u, part, total;
 };
+
+FfnArgs ffn_shape(const moe_config_t* c, int64_t T);
 
 Layout layout(const moe_config_t* c, int64_t T) {
   const int64_t E = c->n_routed_experts, k = c->num_experts_per_tok, H = c->hidden_size;
@@ -156,6 +158,10 @@ Layout layout(const moe_config_t* c, int64_t T) {
   L.y = take(T * k * H * asz);
   L.ysh = take(T * H * asz);
   L.u = take(T * H * asz);
+  {
+    const FfnArgs f = ffn_shape(c, T);
+    L.part = take(ffn_plan(f, c->weight_dtype, c->act_dtype).part_bytes(T, f.k, f.H, f.F, f.Fs));
+  }
   L.total = off;
   return L;
 }
@@ -260,6 +266,9 @@ moe_status_t run_ffn(const moe_config_t* c, const moe_weights_t* w, FfnArgs& f, 
   const int bm = plan.bm;
   f.bm = bm;
   f.kind = plan.kind;
+  f.ks_gu = plan.ks_gu;
+  f.ks_dn = plan.ks_dn;
+  f.part = at<float>(ws, L.part);
   f.tiles = at<Tile>(ws, L.tiles);
   f.tile_count = at<int32_t>(ws, L.tcount);
   f.tile_bound = max_tiles(T, f.k, f.E, f.Fs > 0, bm);
@@ -292,8 +301,8 @@ moe_status_t run_ffn(const moe_config_t* c, const moe_weights_t* w, FfnArgs& f, 
   return MOE_OK;
 }
 
-FfnArgs ffn_args(const moe_config_t* c, int64_t T, void* ws) {
-  const Layout L = layout(c, T);
+// the shape fields of the FFN arguments (what ffn_plan reads)
+FfnArgs ffn_shape(const moe_config_t* c, int64_t T) {
   FfnArgs f{};
   f.T = static_cast<int>(T);
   f.k = c->num_experts_per_tok;
@@ -301,6 +310,12 @@ FfnArgs ffn_args(const moe_config_t* c, int64_t T, void* ws) {
   f.H = c->hidden_size;
   f.F = c->moe_intermediate_size;
   f.Fs = shared_F(c);
+  return f;
+}
+
+FfnArgs ffn_args(const moe_config_t* c, int64_t T, void* ws) {
+  const Layout L = layout(c, T);
+  FfnArgs f = ffn_shape(c, T);
   f.h = at<void>(ws, L.h);
   f.h_sh = at<void>(ws, L.hsh);
   f.hq = at<void>(ws, L.hq);

@@ -304,8 +304,8 @@ namespace moe {
 // Measured on MI355X over Kimi-K2 decode (T = 128..1024), the DeepSeek-V3
 // and Moonlight shapes, expert-parallel rank shares and the dense layer:
 //  * LDS-tiled MFMA kernels (128 rows x 512 or 256 weight rows per block) from
-//    32 rows per expert on, while the down projection's tiled grid still has
-//    64 blocks or more (a single 7168-wide dense layer at 128 tokens has 14);
+//    32 rows per expert on; when that grid is small (few, fat experts) the K
+//    loop is split over up to 8 (gate_up) or 16 (down) blocks;
 //  * else the weight-streaming kernels with work items of 16 rows below 6
 //    rows per expert, 32 below 12 and 64 beyond (an expert of up to 64 rows
 //    then streams its weights once; 128-row items run at half occupancy and
@@ -318,9 +318,17 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   if (weight_dtype == MOE_FP8_E4M3)
     return many_rows && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? FfnPlan{tile_fp8_rows(), FfnPlan::kTiled}
                                                            : FfnPlan{fp8_tile_rows(), FfnPlan::kStream};
-  const int64_t tiled_items = (rows + 127) / 128 + (a.Fs > 0 ? (a.T + 127) / 128 : 0);
-  if (many_rows && tile_shapes_ok(a.H, a.F, a.Fs) && tiled_items * (a.H / 512) >= 64)
-    return {tile_rows(), FfnPlan::kTiled};
+  if (many_rows && tile_shapes_ok(a.H, a.F, a.Fs)) {
+    // few work items (few, fat experts: one expert-parallel rank, the dense
+    // layer) split the K loop so that the grid still fills the chip
+    FfnPlan p{tile_rows(), FfnPlan::kTiled};
+    // expected work items with the rows spread evenly over the experts
+    const int64_t per_e = (rows + a.E - 1) / a.E;
+    const int64_t items = a.E * ((per_e + 127) / 128) + (a.Fs > 0 ? (a.T + 127) / 128 : 0);
+    p.ks_gu = tile_ksplit(items * (std::max(a.F, a.Fs) / 256), a.H, a.H, 8, 256);
+    p.ks_dn = tile_ksplit(items * (a.H / 512), a.F, a.Fs > 0 ? a.Fs : a.F, 16, 128);
+    return p;
+  }
   const int bm = per_expert < 6.0 ? 16 : (per_expert < 12.0 ? 32 : 64);
   return {bm, FfnPlan::kStream};
 }

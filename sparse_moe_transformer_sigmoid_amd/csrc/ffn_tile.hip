@@ -63,19 +63,24 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
 
 // MODE 0: gate_up (K = H, slab = 256 features = 256 gate + 256 up rows)
 // MODE 1: down    (K = F or Fs, slab = 512 output rows)
+// `ks` > 1 splits the K loop over ks blocks (few work items): each writes its
+// fp32 partial sums to a.part, and ffn_split_finish adds them up in part
+// order and applies the epilogue.
 template <int MODE>
-__global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs) {
+__global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int ks) {
   // two stages as separate objects: the compiler then knows that a DMA into
   // one stage does not alias LDS reads of the other
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
-  // ---- XCD-chunked mapping of this block to (slab, tile) ----
+  // ---- XCD-chunked mapping of this block to (K part, slab, tile) ----
   const int ntile = *a.tile_count;
-  const int total = slabs * ntile;
+  const int total = slabs * ntile * ks;
   const int per = (total + kXcd - 1) / kXcd;
   const int j = blockIdx.x / kXcd;
-  const int v = (blockIdx.x % kXcd) * per + j;
-  if (j >= per || v >= total) return;
+  const int v0 = (blockIdx.x % kXcd) * per + j;
+  if (j >= per || v0 >= total) return;
+  const int kp = v0 / (slabs * ntile);
+  const int v = v0 - kp * (slabs * ntile);
   const int slab = v / ntile;
   const Tile tl = a.tiles[v - slab * ntile];
   const bool sh = tl.group == a.E;
@@ -150,7 +155,8 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
 
-  const int steps = K / kBK;   // even (K is a multiple of 128)
+  // this block's K steps [s0, s0 + steps); steps is even
+  const int steps = K / kBK / ks, s0 = kp * steps;
   const int sw = (r32 >> 1) & 7;                       // row swizzle of this lane's rows
   const int arow = (128 * wave + r32) * kRowB;
   const int brow = (kBW + r32) * kRowB;
@@ -200,12 +206,36 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs) {
   };
 
 #pragma unroll
-  for (int g = 0; g < 20; ++g) dma(g, 0, st0);
+  for (int g = 0; g < 20; ++g) dma(g, s0, st0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int s = 0; s < steps; s += 2) {
-    step(st0, st1, s + 1);
-    step(st1, st0, min(s + 2, steps - 1));
+    step(st0, st1, s0 + s + 1);
+    step(st1, st0, s0 + min(s + 2, steps - 1));
+  }
+
+  if (ks > 1) {
+    // ---- partial sums: row p of part kp holds gate | up (gate_up, width
+    // 2 * max(F, Fs)) or the output row (down, width H), fp32 ----
+    const int64_t R = TK + a.T;
+    const int width = MODE == 0 ? 2 * max(a.F, a.Fs) : a.H;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int tr = 32 * n + r32;
+      if (tr >= tl.rows) continue;
+      float* dst = a.part + (static_cast<int64_t>(kp) * R + tl.row0 + tr) * width;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        // gate_up: m = 0, 1 gate features, 2, 3 the same features' up rows
+        const int col = MODE == 0 ? (m >> 1) * (width / 2) + o0 + 64 * wave + 32 * (m & 1)
+                                  : o0 + 128 * wave + 32 * m;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(dst + col + 8 * g + 4 * kh) =
+              make_float4(acc[m][n][4 * g], acc[m][n][4 * g + 1], acc[m][n][4 * g + 2], acc[m][n][4 * g + 3]);
+      }
+    }
+    return;
   }
 
   // ---- epilogue: lane holds rows 8*(i/4) + 4*kh + (i%4) of each 32-row
@@ -248,7 +278,58 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs) {
   }
 }
 
+// Sum of the K-part partials of each grouped row in part order, then the
+// epilogue: SiLU(gate) * up to h (gate_up) or the output row to y (down).
+// One block per grouped row; routed rows past offsets[E] (unused capacity)
+// and rows of no group are skipped.
+template <int MODE>
+__global__ __launch_bounds__(256) void ffn_split_finish(FfnArgs a, int ks) {
+  const int64_t p = blockIdx.x;
+  const int64_t TK = static_cast<int64_t>(a.T) * a.k, R = TK + a.T;
+  const bool sh = p >= TK;
+  if (sh ? a.Fs == 0 : p >= a.offsets[a.E]) return;
+  const int Fg = sh ? a.Fs : a.F;
+  const int width = MODE == 0 ? 2 * max(a.F, a.Fs) : a.H;
+  const int n4 = (MODE == 0 ? Fg : a.H) / 4;
+  for (int c = threadIdx.x; c < n4; c += blockDim.x) {
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+    for (int kp = 0; kp < ks; ++kp) {
+      const float* src = a.part + (static_cast<int64_t>(kp) * R + p) * width;
+      const float4 x = reinterpret_cast<const float4*>(src)[c];
+      g.x += x.x; g.y += x.y; g.z += x.z; g.w += x.w;
+      if (MODE == 0) {
+        const float4 y = reinterpret_cast<const float4*>(src + width / 2)[c];
+        u.x += y.x; u.y += y.y; u.z += y.z; u.w += y.w;
+      }
+    }
+    uint2 v2;
+    if (MODE == 0) {
+      v2.x = pack_bf16(silu(g.x) * u.x, silu(g.y) * u.y);
+      v2.y = pack_bf16(silu(g.z) * u.z, silu(g.w) * u.w);
+      uint16_t* dst = sh ? static_cast<uint16_t*>(a.h_sh) + (p - TK) * a.Fs : static_cast<uint16_t*>(a.h) + p * a.F;
+      reinterpret_cast<uint2*>(dst)[c] = v2;
+    } else {
+      v2.x = pack_bf16(g.x, g.y);
+      v2.y = pack_bf16(g.z, g.w);
+      uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (p - TK) * a.H : static_cast<uint16_t*>(a.y) + p * a.H;
+      reinterpret_cast<uint2*>(dst)[c] = v2;
+    }
+  }
+}
+
 int tile_rows() { return kBM; }
+
+// K parts of the tiled kernels for a grid of `blocks` (slabs x work items):
+// doubled (up to max_ks) while the grid has fewer than `target` blocks (the
+// kernel holds a whole CU's LDS, so 256 blocks fill the chip), keeping every
+// part an even number of 64-wide steps of both K1 and K2.  Measured: gate_up
+// gains up to 256 blocks; down, whose partial sums are 7168 wide, only below
+// 128 (at 140 blocks the extra pass cost more than the split gained).
+int tile_ksplit(int64_t blocks, int K1, int K2, int max_ks, int target) {
+  int ks = 1;
+  while (ks < max_ks && blocks * ks < target && (K1 / kBK) % (4 * ks) == 0 && (K2 / kBK) % (4 * ks) == 0) ks *= 2;
+  return ks;
+}
 
 // slabs must divide the weight dimensions: F, Fs by 256, H by 512
 bool tile_shapes_ok(int H, int F, int Fs) {
@@ -256,19 +337,23 @@ bool tile_shapes_ok(int H, int F, int Fs) {
 }
 
 template <int MODE>
-static hipError_t launch_tile(const FfnArgs& a, int slabs, hipStream_t st) {
-  const int64_t blocks = static_cast<int64_t>(slabs) * a.tile_bound;
+static hipError_t launch_tile(const FfnArgs& a, int slabs, int ks, hipStream_t st) {
+  const int64_t blocks = static_cast<int64_t>(slabs) * a.tile_bound * ks;
   hipLaunchKernelGGL((ffn_tile_bf16<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
-                     slabs);
+                     slabs, ks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  const int64_t rows = static_cast<int64_t>(a.T) * a.k + a.T;
+  hipLaunchKernelGGL((ffn_split_finish<MODE>), dim3(static_cast<unsigned>(rows)), dim3(256), 0, st, a, ks);
   return hipGetLastError();
 }
 
 hipError_t launch_gate_up_tile(const FfnArgs& a, hipStream_t st) {
-  return launch_tile<0>(a, std::max(a.F, a.Fs) / (kBW / 2), st);
+  return launch_tile<0>(a, std::max(a.F, a.Fs) / (kBW / 2), a.ks_gu, st);
 }
 
 hipError_t launch_down_tile(const FfnArgs& a, hipStream_t st) {
-  return launch_tile<1>(a, a.H / kBW, st);
+  return launch_tile<1>(a, a.H / kBW, a.ks_dn, st);
 }
 
 }  // namespace moe

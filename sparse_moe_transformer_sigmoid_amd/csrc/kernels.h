@@ -64,6 +64,8 @@ struct FfnArgs {
   int64_t tile_bound;  // grid size along tiles
   int bm;              // rows per tile used to build `tiles`
   int kind;            // FfnPlan::Kind of the kernels to launch
+  int ks_gu, ks_dn;    // K parts of the tiled gate_up / down (1: no split)
+  float* part;         // fp32 partial sums [ks][T*k + T][width] when a K part count > 1
   const int32_t* offsets;  // [E+1] (simple fp32 kernels)
   // weights (dtype per mode); routed [E][F][H] / [E][H][F], shared [Fs][H] / [H][Fs]
   const void *w_gate, *w_up, *w_down, *sh_gate, *sh_up, *sh_down;
@@ -93,6 +95,13 @@ struct FfnPlan {
   enum Kind { kSimple = 0, kStream = 1, kTiled = 2 };
   int bm;    // rows per work-list tile
   int kind;
+  int ks_gu = 1, ks_dn = 1;  // K parts of the tiled bf16 kernels
+  // bytes of fp32 partial sums the K parts need (0 without a split)
+  int64_t part_bytes(int64_t T, int k, int H, int F, int Fs) const {
+    const int64_t R = T * k + T, Fm = F > Fs ? F : Fs;
+    const int64_t a = ks_gu > 1 ? ks_gu * R * 2 * Fm : 0, b = ks_dn > 1 ? ks_dn * R * H : 0;
+    return 4 * (a > b ? a : b);
+  }
 };
 FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype);
 bool tile_shapes_ok(int H, int F, int Fs);
@@ -106,6 +115,7 @@ int fp8_tile_rows();
 hipError_t launch_gate_up_tile(const FfnArgs& a, hipStream_t st);  // ffn_tile.hip
 hipError_t launch_down_tile(const FfnArgs& a, hipStream_t st);
 int tile_rows();
+int tile_ksplit(int64_t blocks, int K1, int K2, int max_ks, int target);
 
 // pre-MoE RMSNorm, fp64, rounded once to the activation dtype into u [T][H];
 // with `codes` (bf16 only) also the fp8 quantisation of u (codes [T][H],
