@@ -4,7 +4,9 @@
 One step = one moe_layer_forward (router, grouping, expert FFNs, combine) over
 one batch of synthetic tokens whose inputs are already resident in HBM.
 Default workload: Kimi-K2 decode, T = 128 tokens, bf16, all 384 experts + 1
-shared resident.  For an expert-parallel rank workload (ep_size > 1) a step
+shared resident.  A step is captured once in a HIP graph and replayed (the
+library only launches kernels: no memset, no host synchronisation); --eager
+launches every step from the host instead.  For an expert-parallel rank workload (ep_size > 1) a step
 is that rank's expert FFN share (moe_expert_ffn over the rows dispatched to
 its local experts plus the shared expert over its own tokens), and value is
 the rank's own tokens per second.  For a sub-block workload (block) a step is
@@ -229,11 +231,35 @@ def make_step(cfg, weights, wl, case, T):
     return step, ids
 
 
+def graphed(step):
+    """One step captured in a HIP graph (the library launches kernels only);
+    returns a callable that replays it."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    torch.cuda.synchronize()
+    return g.replay
+
+
+GRAPH = False
+
+
 def measure(cfg, weights, wl, case, T, steps, warmup, hip, factory=make_step):
     """Time `steps` layer steps after `warmup` untimed ones (synchronised on
     both sides); the gate_up launch of every timed step is bracketed by HIP
-    events the library records on its own stream."""
+    events the library records on its own stream (not with --graph, whose
+    replays record no events: gate_up is then timed on as many eager steps
+    after the graph's timed region)."""
     step, ids = factory(cfg, weights, wl, case, T)
+    eager = step
+    if GRAPH:
+        step = graphed(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -242,11 +268,17 @@ def measure(cfg, weights, wl, case, T, steps, warmup, hip, factory=make_step):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        B.moe_profile_arm(B.MOE_KID_GATE_UP, *evs[i])
+        if not GRAPH:
+            B.moe_profile_arm(B.MOE_KID_GATE_UP, *evs[i])
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))  # every step launches it
+    if GRAPH:
+        for i in range(steps):
+            B.moe_profile_arm(B.MOE_KID_GATE_UP, *evs[i])
+            eager()
+        torch.cuda.synchronize()
+    gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))  # every eager step launches it
     return step, wall, gate_up_ms, n_active
 
 
@@ -293,6 +325,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--extra-out", default=None, help="append a detail JSON line to this file")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from the host instead of replaying one captured HIP graph")
     ap.add_argument("--sweep-tokens", default=None,
                     help="comma-separated token counts measured after the main line (stderr / --extra-out)")
     args = ap.parse_args()
@@ -306,6 +340,8 @@ def main():
 
     wl = gen.WORKLOADS[args.workload]
     T = args.tokens or wl.num_tokens
+    global GRAPH
+    GRAPH = not args.eager
     B.load()
     hip = Hip()
     rank = wl.ep_size > 1
@@ -363,7 +399,8 @@ def main():
                    "moe_intermediate_size": wl.moe_intermediate_size, "n_routed_experts": wl.n_routed_experts,
                    "num_experts_per_tok": wl.num_experts_per_tok, "n_shared_experts": wl.n_shared_experts,
                    "n_group": wl.n_group, "topk_group": wl.topk_group, "active_experts": n_active,
-                   "parallelism": "none (one GPU, all experts resident)"},
+                   "parallelism": "none (one GPU, all experts resident)",
+                   "launch": "eager" if args.eager else "hip graph replay (one captured layer step)"},
         "roofline": rl,
     }
     if rank:

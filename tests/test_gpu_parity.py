@@ -345,3 +345,56 @@ def test_k2_block_fp8_full_size(k2_fp8_weights):
     err = block_err(out[torch.as_tensor(tokens, device="cuda")], ref, cases.to64(case["x"])[tokens], wl.act_dtype)
     say(f"  sampled tokens {list(tokens)}: err {err:.3e}")
     assert err <= TOL[wl.weight_dtype]
+
+
+# ----------------------------------------------------------- graph capture --
+@pytest.mark.parametrize("name,block", [("small_bf16", False), ("small_fp8", False), ("small_bf16", True)])
+def test_layer_replays_from_a_graph(name, block):
+    """The entry points launch kernels only (no memset, no host sync), so a
+    call can be captured in a HIP graph: every replay -- with eager library
+    calls and a change of input between replays -- equals the eager result
+    on the same input, bit for bit."""
+    wl = W[name]
+    T = 100
+    case = cases.make_block_case(wl, device="cuda", num_tokens=T) if block else small_case(wl, T)
+    cfg = B.MoeConfig.from_fields(wl.fields())
+    weights = B.MoeWeights.from_tensors(case)
+    eps = float(np.float32(wl.rms_norm_eps))
+    x = case["x"].clone()
+    out = torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda")
+    ids = torch.empty((T, wl.num_experts_per_tok), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, wl.num_experts_per_tok), dtype=torch.float32, device="cuda")
+    ws = B.alloc_workspace(cfg, T)
+
+    def call():
+        if block:
+            B.moe_block_forward(cfg, weights, x, case["norm_weight"], eps, case["router_w"], case["router_bias"],
+                                out, ws, ids, wts)
+        else:
+            B.moe_layer_forward(cfg, weights, x, case["router_w"], case["router_bias"], out, ws, ids, wts)
+
+    def eager(xin):
+        c = dict(case)
+        c["x"] = xin
+        return (run_block if block else run_layer)(wl, c)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        call()
+    torch.cuda.synchronize()
+    inputs = [case["x"], case["x"].flip(0).contiguous(), case["x"]]
+    for i, xin in enumerate(inputs + inputs):
+        x.copy_(xin)
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_ids, ref_w = eager(xin.clone())   # eager work between replays
+        say(f"  replay {i}: equal={torch.equal(out, ref_out)}")
+        assert torch.equal(out, ref_out) and torch.equal(ids, ref_ids) and torch.equal(wts, ref_w)
