@@ -279,7 +279,7 @@ def measure(cfg, weights, wl, case, T, steps, warmup, hip, factory=make_step):
             eager()
         torch.cuda.synchronize()
     gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))  # every eager step launches it
-    return step, wall, gate_up_ms, n_active
+    return eager, wall, gate_up_ms, n_active
 
 
 def layer_bytes(wl, T, n_active):
