@@ -300,25 +300,27 @@ hipError_t launch_simple_f32(const FfnArgs& a, bool gate_up, hipStream_t st) {
 namespace moe {
 
 // Rows per work-list tile and the kernel family of one call, from the
-// expected rows per expert (T*k / E; the row capacity for one rank's share).
-// Measured on MI355X over Kimi-K2 decode (T = 128..1024), the DeepSeek-V3
-// and Moonlight shapes, expert-parallel rank shares and the dense layer:
-//  * LDS-tiled MFMA kernels (128 rows x 512 or 256 weight rows per block) from
-//    32 rows per expert on; when that grid is small (few, fat experts) the K
-//    loop is split over up to 8 (gate_up) or 16 (down) blocks;
-//  * else the weight-streaming kernels with work items of 16 rows below 6
-//    rows per expert, 32 below 12 and 64 beyond (an expert of up to 64 rows
-//    then streams its weights once; 128-row items run at half occupancy and
-//    were slower in every case).
+// expected rows per expert r = T*k / E (the row capacity for one rank's
+// share).  Measured on MI355X over Kimi-K2 decode (T = 128..1024), the
+// DeepSeek-V3 and Moonlight shapes, expert-parallel rank shares and the dense
+// layer (whole-layer time, tiled vs streamed: T=256, r=5: 5.84 vs 5.65 ms;
+// T=512, r=11: 6.15 vs 6.84; T=1024, r=21: 6.48 vs 8.32):
+//  * bf16 from r = 8 on: the LDS-tiled MFMA kernels (128 rows x 512 weight
+//    rows per block); when that grid is small (few, fat experts) the K loop
+//    is split over up to 8 (gate_up) or 16 (down) blocks;
+//  * below, or when the shapes do not fit the tiles: the weight-streaming
+//    kernels with work items of 16 rows below 6 rows per expert, 32 below 12
+//    and 64 beyond (128-row items run at half occupancy and were slower in
+//    every case);
+//  * fp8: the fp8 tiled kernel from r = 32 on, else its streaming kernel.
 FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   if (act_dtype == MOE_F32) return {16, FfnPlan::kSimple};
   const int64_t rows = static_cast<int64_t>(a.T) * a.k;
   const double per_expert = static_cast<double>(rows) / a.E;
-  const bool many_rows = per_expert >= 32.0;
   if (weight_dtype == MOE_FP8_E4M3)
-    return many_rows && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? FfnPlan{tile_fp8_rows(), FfnPlan::kTiled}
-                                                           : FfnPlan{fp8_tile_rows(), FfnPlan::kStream};
-  if (many_rows && tile_shapes_ok(a.H, a.F, a.Fs)) {
+    return per_expert >= 32.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? FfnPlan{tile_fp8_rows(), FfnPlan::kTiled}
+                                                                   : FfnPlan{fp8_tile_rows(), FfnPlan::kStream};
+  if (per_expert >= 8.0 && tile_shapes_ok(a.H, a.F, a.Fs)) {
     // few work items (few, fat experts: one expert-parallel rank, the dense
     // layer) split the K loop so that the grid still fills the chip
     FfnPlan p{tile_rows(), FfnPlan::kTiled};

@@ -338,7 +338,9 @@ bool tile_shapes_ok(int H, int F, int Fs) {
 
 template <int MODE>
 static hipError_t launch_tile(const FfnArgs& a, int slabs, int ks, hipStream_t st) {
-  const int64_t blocks = static_cast<int64_t>(slabs) * a.tile_bound * ks;
+  // a multiple of 8: block b serves item (b % 8) * per + b / 8 with
+  // per = ceil(items / 8), which needs 8 * per blocks to reach every item
+  const int64_t blocks = (static_cast<int64_t>(slabs) * a.tile_bound * ks + kXcd - 1) / kXcd * kXcd;
   hipLaunchKernelGGL((ffn_tile_bf16<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
                      slabs, ks);
   hipError_t e = hipGetLastError();

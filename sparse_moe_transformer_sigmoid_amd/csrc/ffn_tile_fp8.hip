@@ -304,7 +304,9 @@ bool tile_fp8_shapes_ok(int H, int F, int Fs) {
 
 template <int MODE>
 static hipError_t launch_tile_fp8(const FfnArgs& a, int slabs, hipStream_t st) {
-  const int64_t blocks = static_cast<int64_t>(slabs) * a.tile_bound;
+  // a multiple of 8: block b serves item (b % 8) * per + b / 8 with
+  // per = ceil(items / 8), which needs 8 * per blocks to reach every item
+  const int64_t blocks = (static_cast<int64_t>(slabs) * a.tile_bound + kXcd - 1) / kXcd * kXcd;
   hipLaunchKernelGGL((ffn_tile_fp8<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, a,
                      slabs);
   return hipGetLastError();
