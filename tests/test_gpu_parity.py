@@ -401,3 +401,16 @@ def test_layer_replays_from_a_graph(name, block):
         ref_out, ref_ids, ref_w = eager(xin.clone())   # eager work between replays
         say(f"  replay {i}: equal={torch.equal(out, ref_out)}")
         assert torch.equal(out, ref_out) and torch.equal(ids, ref_ids) and torch.equal(wts, ref_w)
+
+
+def test_k2_max_tokens_full_size(k2_weights):
+    """The largest batch the ABI takes (65536 tokens, 524288 grouped rows:
+    row offsets past 2^31 elements): routing of every token and the
+    grouping are exact; sampled rows match the oracle."""
+    wl = W["k2_prefill_bf16_zipf"]
+    T = 65536
+    case = full_case(wl, k2_weights, T)
+    out, ids, w = run_layer(wl, case)
+    route = full_route(wl, case)
+    check_route(ids, w, route)
+    check_sampled(wl, case, out, [0, T // 2 - 1, T - 1])
