@@ -92,9 +92,17 @@ def test_stages_match_oracle_and_layer(name):
     assert torch.equal(out, r["out"]), "stage chain and fused layer differ"
 
 
-def test_layer_is_deterministic():
-    wl = W["small_bf16"]
-    case = small_case(wl, 300)
+@pytest.mark.parametrize("name,T", [("small_bf16", 300), ("small_bf16", 7), ("small_fp8", 300),
+                                    ("small_grouped_bf16", 100), ("tiny_fp32", 37)])
+def test_every_stage_is_deterministic(name, T):
+    """Each stage run twice gives the same bits (fixed-order reductions, stable
+    grouping, K-split partials added in part order), and so does the layer."""
+    wl = W[name]
+    case = small_case(wl, T)
+    r1, r2 = run_stages(wl, case), run_stages(wl, case)
+    for key, v in r1.items():
+        if v is not None:
+            assert torch.equal(v, r2[key]), f"stage output {key} differs between runs"
     a, ia, wa = run_layer(wl, case)
     b, ib, wb = run_layer(wl, case)
     assert torch.equal(a, b) and torch.equal(ia, ib) and torch.equal(wa, wb)
