@@ -239,8 +239,12 @@ moe_status_t run_route(const moe_config_t* c, const void* x, const void* rw, con
   return MOE_OK;
 }
 
+// `ft` (nullable): FFN arguments whose plan is already set (ffn_prepare); the
+// single-block grouping of small batches then also writes their work list and
+// `*tiles_built` says so
 moe_status_t run_permute(const moe_config_t* c, const int32_t* ids, int64_t T, int32_t* offsets,
-                         int32_t* sorted, int32_t* inv, bool tail, void* ws, hipStream_t st) {
+                         int32_t* sorted, int32_t* inv, bool tail, void* ws, hipStream_t st,
+                         const FfnArgs* ft = nullptr, bool* tiles_built = nullptr) {
   const Layout L = layout(c, T);
   PermArgs p{};
   p.ids = ids;
@@ -253,14 +257,20 @@ moe_status_t run_permute(const moe_config_t* c, const int32_t* ids, int64_t T, i
   p.sorted = sorted;
   p.inv = inv;
   p.identity_tail = tail;
-  // the three grouping kernels are timed as one unit
-  MOE_LAUNCH(MOE_KID_PERMUTE, launch_permute(p, st));
+  if (ft) {
+    p.tiles = const_cast<Tile*>(ft->tiles);
+    p.tile_count = const_cast<int32_t*>(ft->tile_count);
+    p.bm = ft->bm;
+    p.shared = ft->Fs > 0;
+    p.cap = ft->tile_bound;
+  }
+  // the grouping kernels are timed as one unit
+  MOE_LAUNCH(MOE_KID_PERMUTE, launch_permute(p, st, tiles_built));
   return MOE_OK;
 }
 
-// gate_up + down over a work list built from `offsets`
-moe_status_t run_ffn(const moe_config_t* c, const moe_weights_t* w, FfnArgs& f, int64_t T,
-                     void* ws, hipStream_t st) {
+// the plan and work-list fields of the FFN arguments
+moe_status_t ffn_prepare(const moe_config_t* c, FfnArgs& f, int64_t T, void* ws) {
   const Layout L = layout(c, T);
   const FfnPlan plan = ffn_plan(f, c->weight_dtype, c->act_dtype);
   const int bm = plan.bm;
@@ -273,6 +283,14 @@ moe_status_t run_ffn(const moe_config_t* c, const moe_weights_t* w, FfnArgs& f, 
   f.tile_count = at<int32_t>(ws, L.tcount);
   f.tile_bound = max_tiles(T, f.k, f.E, f.Fs > 0, bm);
   if (f.tile_bound > 65535) return fail(MOE_ERR_UNSUPPORTED, "too many tiles (%lld) for one launch", (long long)f.tile_bound);
+  return MOE_OK;
+}
+
+// gate_up + down over a work list built from `offsets` (`tiles_ready`: the
+// list is already built, ffn_prepare already ran)
+moe_status_t run_ffn(const moe_config_t* c, const moe_weights_t* w, FfnArgs& f, int64_t T,
+                     void* ws, hipStream_t st, bool tiles_ready = false) {
+  if (!tiles_ready) TRY(ffn_prepare(c, f, T, ws));
   f.w_gate = w->w_gate;
   f.w_up = w->w_up;
   f.w_down = w->w_down;
@@ -290,12 +308,12 @@ moe_status_t run_ffn(const moe_config_t* c, const moe_weights_t* w, FfnArgs& f, 
   ta.T = f.T;
   ta.k = f.k;
   ta.E = f.E;
-  ta.bm = bm;
+  ta.bm = f.bm;
   ta.shared = f.Fs > 0;
   ta.cap = f.tile_bound;
   ta.tiles = const_cast<Tile*>(f.tiles);
   ta.tile_count = const_cast<int32_t*>(f.tile_count);
-  MOE_LAUNCH(MOE_KID_TILES, launch_build_tiles(ta, st));
+  if (!tiles_ready) MOE_LAUNCH(MOE_KID_TILES, launch_build_tiles(ta, st));
   MOE_LAUNCH(MOE_KID_GATE_UP, launch_gate_up(f, c->act_dtype, c->weight_dtype, st));
   MOE_LAUNCH(MOE_KID_DOWN, launch_down(f, c->act_dtype, c->weight_dtype, st));
   return MOE_OK;
@@ -355,8 +373,10 @@ moe_status_t run_layer(const moe_config_t* cfg, const moe_weights_t* w, const vo
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* rows = at<int32_t>(ws, L.rows);
   int32_t* inv = at<int32_t>(ws, L.inv);
-  TRY(run_permute(cfg, ids, T, offsets, rows, inv, true, ws, st));
   FfnArgs f = ffn_args(cfg, T, ws);
+  TRY(ffn_prepare(cfg, f, T, ws));
+  bool tiles_ready = false;
+  TRY(run_permute(cfg, ids, T, offsets, rows, inv, true, ws, st, &f, &tiles_ready));
   f.offsets = offsets;
   f.xr = x;
   f.xr_rows = rows;
@@ -373,7 +393,7 @@ moe_status_t run_layer(const moe_config_t* cfg, const moe_weights_t* w, const vo
     f.xs = xq;
     f.xs_scales = xs;
   }
-  TRY(run_ffn(cfg, w, f, T, ws, st));
+  TRY(run_ffn(cfg, w, f, T, ws, st, tiles_ready));
   CombineArgs a{f.y, cfg->n_shared_experts > 0 ? f.y_sh : nullptr, wts, inv, static_cast<int>(T),
                 cfg->num_experts_per_tok, cfg->hidden_size, out, resid};
   MOE_LAUNCH(MOE_KID_COMBINE, launch_combine(a, cfg->act_dtype == MOE_BF16, st));

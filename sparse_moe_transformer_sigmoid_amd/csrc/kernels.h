@@ -31,8 +31,17 @@ struct PermArgs {
   int32_t* sorted;        // [T*k] (+T identity rows when identity_tail)
   int32_t* inv;           // [T*k]
   bool identity_tail;
+  // optional (tiles != nullptr, T <= kPermChunk): also build the work list of
+  // the grouped GEMMs in the same single-block launch (see TileArgs)
+  Tile* tiles;
+  int32_t* tile_count;
+  int bm, shared;
+  int64_t cap;
 };
-hipError_t launch_permute(const PermArgs& a, hipStream_t st);
+// T <= kPermChunk: one single-block kernel (count, scan, stable scatter and,
+// with `tiles`, the work list); else three kernels.  Returns whether the work
+// list was built.
+hipError_t launch_permute(const PermArgs& a, hipStream_t st, bool* tiles_built = nullptr);
 
 struct TileArgs {
   const int32_t* offsets;  // [E+1]

@@ -106,7 +106,79 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ 
       sorted[static_cast<int64_t>(T) * k + t] = t;
 }
 
-hipError_t launch_permute(const PermArgs& a, hipStream_t st) {
+// The whole grouping for T <= kPermChunk in one block of 1024 threads: the
+// histogram (LDS atomics), the exclusive scan over experts (thread e owns
+// expert e), the stable scatter with the same 64-bit token masks as
+// perm_scatter and, optionally, the work list of build_tiles.  Small batches
+// (decode) are bound by launch latency, so one launch instead of four.
+__global__ __launch_bounds__(1024) void perm_single(PermArgs a) {
+  extern __shared__ unsigned long long smem[];
+  unsigned long long* mask = smem;                               // [E]
+  int32_t* run = reinterpret_cast<int32_t*>(smem + a.E);         // [E]
+  const int E = a.E, T = a.T, k = a.k, tid = threadIdx.x;
+  const int n_all = T * k;
+  for (int e = tid; e < E; e += blockDim.x) run[e] = 0;
+  __syncthreads();
+  for (int i = tid; i < n_all; i += blockDim.x) atomicAdd(&run[a.ids[i]], 1);
+  __syncthreads();
+  const int cnt = tid < E ? run[tid] : 0;
+  int all;
+  const int off = block_exclusive_scan(cnt, &all);
+  if (tid < E) {
+    a.offsets[tid] = off;
+    run[tid] = off;
+  }
+  if (tid == 0) a.offsets[E] = n_all;
+  __syncthreads();
+  for (int g0 = 0; g0 < T; g0 += 64) {
+    for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
+    __syncthreads();
+    const int n = min(64, T - g0) * k;
+    for (int i = tid; i < n; i += blockDim.x) atomicOr(&mask[a.ids[g0 * k + i]], 1ull << (i / k));
+    __syncthreads();
+    for (int i = tid; i < n; i += blockDim.x) {
+      const int tl = i / k, flat = g0 * k + i, e = a.ids[flat];
+      const int pos = run[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
+      a.sorted[pos] = g0 + tl;
+      a.inv[flat] = pos;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) run[e] += __popcll(mask[e]);
+    __syncthreads();
+  }
+  if (a.identity_tail)
+    for (int t = tid; t < T; t += blockDim.x) a.sorted[n_all + t] = t;
+  if (a.tiles == nullptr) return;
+  // work list: group g < E = expert g (cnt rows from off), group E = shared
+  int n = 0, base = 0;
+  if (tid < E) {
+    n = cnt;
+    base = off;
+  } else if (tid == E && a.shared) {
+    n = T;
+    base = n_all;
+  }
+  const int nt = (n + a.bm - 1) / a.bm;
+  int tiles_all;
+  const int start = block_exclusive_scan(nt, &tiles_all);
+  for (int i = 0; i < nt && start + i < a.cap; ++i) {
+    Tile t;
+    t.group = tid;
+    t.row0 = base + i * a.bm;
+    t.rows = min(a.bm, n - i * a.bm);
+    t.pad = 0;
+    a.tiles[start + i] = t;
+  }
+  if (tid == 0) *a.tile_count = static_cast<int32_t>(min(static_cast<int64_t>(tiles_all), a.cap));
+}
+
+hipError_t launch_permute(const PermArgs& a, hipStream_t st, bool* tiles_built) {
+  if (tiles_built) *tiles_built = false;
+  if (a.T <= kPermChunk) {
+    hipLaunchKernelGGL(perm_single, dim3(1), dim3(1024), a.E * (sizeof(unsigned long long) + 4), st, a);
+    if (tiles_built) *tiles_built = a.tiles != nullptr;
+    return hipGetLastError();
+  }
   const int nchunk = (a.T + kPermChunk - 1) / kPermChunk;
   hipLaunchKernelGGL(perm_count, dim3(nchunk), dim3(256), a.E * sizeof(int32_t), st, a.ids, a.T,
                      a.k, a.E, a.chunk_counts);
