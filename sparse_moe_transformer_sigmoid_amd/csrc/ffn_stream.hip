@@ -320,7 +320,7 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   if (weight_dtype == MOE_FP8_E4M3)
     return per_expert >= 32.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? FfnPlan{tile_fp8_rows(), FfnPlan::kTiled}
                                                                    : FfnPlan{fp8_tile_rows(), FfnPlan::kStream};
-  if (per_expert >= 8.0 && tile_shapes_ok(a.H, a.F, a.Fs)) {
+  if (per_expert >= 8.0 && tile_shapes_ok(a.T, a.H, a.F, a.Fs)) {
     // few work items (few, fat experts: one expert-parallel rank, the dense
     // layer) split the K loop so that the grid still fills the chip
     FfnPlan p{tile_rows(), FfnPlan::kTiled};

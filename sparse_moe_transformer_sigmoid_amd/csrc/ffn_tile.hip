@@ -14,15 +14,19 @@
 //  * down: a wave owns 128 output rows.
 // Both operands go global -> LDS by DMA (global_load_lds_dwordx4, no VGPR
 // staging), 64 K-elements (128 B per row) per step, two 80 KB stages (the
-// whole 160 KB LDS).  Rows are unpadded; 16-byte slot = chunk ^ ((row >> 1)
+// whole 160 KB LDS).  Each DMA source is a wave-uniform base in scalar
+// registers plus a 32-bit lane offset (the instruction's SADDR form), so an
+// issue costs no 64-bit vector address arithmetic.  Rows are unpadded; 16-byte slot = chunk ^ ((row >> 1)
 // & 7), because with 128-byte rows the 64 banks give bank group 8*(row%2) +
 // slot and a 128-bit read serves 16 lanes per cycle, so any 16 consecutive
 // rows land in distinct groups.  The grouped rows are gathered by the DMA
 // itself through the row -> token map.
 // A K step is 4 sub-steps of 16 K-elements (16 MFMAs each per wave); the
 // fragments of sub-step i+1 are read from LDS while sub-step i computes, and
-// the 20 DMA issues of the next step are spread over the first three
-// sub-steps; then wait + barrier.  The two stages are separate __shared__
+// the 20 DMA issues of the next step go out early, evenly among the MFMAs of
+// the first two sub-steps (a batch takes about one step's time to land at
+// full load, so late issues stall the end-of-step wait); then wait +
+// barrier.  The two stages are separate __shared__
 // objects and the step loop is unrolled by two, so the compiler can see that
 // the DMA into one stage never aliases the reads of the other and places no
 // wait for it in front of them.
@@ -86,17 +90,19 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
   const bool sh = tl.group == a.E;
   const int Fg = sh ? a.Fs : a.F;
   const int64_t TK = static_cast<int64_t>(a.T) * a.k;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, kh = lane >> 5;
   // DMA lane geometry: one wave instruction fills 8 LDS rows (1 KB); lane ->
   // row (lane >> 3) of that group, slot (lane & 7), which must hold global
   // chunk slot ^ f(row); f changes by 4 between even and odd 8-row groups
   const int drow = lane >> 3;
   const int dch[2] = {(lane & 7) ^ ((drow >> 1) & 7), (lane & 7) ^ ((4 + (drow >> 1)) & 7)};
+  // DMA sources: wave-uniform bases plus 32-bit lane byte offsets
 
   // ---- weight rows of this wave: two 64-row halves ----
   int K, o0;
-  const uint8_t* wb[2];
+  const uint8_t* wsb[2];
   if (MODE == 0) {
     K = a.H;
     o0 = slab * (kBW / 2);
@@ -104,46 +110,49 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
     const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.F * a.H;
     const uint16_t* wg = static_cast<const uint16_t*>(sh ? a.sh_gate : a.w_gate) + wofs;
     const uint16_t* wu = static_cast<const uint16_t*>(sh ? a.sh_up : a.w_up) + wofs;
-    const int64_t f = o0 + 64 * wave + drow;
-    wb[0] = reinterpret_cast<const uint8_t*>(wg + f * K);
-    wb[1] = reinterpret_cast<const uint8_t*>(wu + f * K);
+    const int64_t f = o0 + 64 * wave;
+    wsb[0] = reinterpret_cast<const uint8_t*>(wg + f * K);
+    wsb[1] = reinterpret_cast<const uint8_t*>(wu + f * K);
   } else {
     K = Fg;
     o0 = slab * kBW;
     const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.H * a.F;
     const uint16_t* wd = static_cast<const uint16_t*>(sh ? a.sh_down : a.w_down) + wofs;
-    const int64_t r = o0 + 128 * wave + drow;
-    wb[0] = reinterpret_cast<const uint8_t*>(wd + r * K);
-    wb[1] = reinterpret_cast<const uint8_t*>(wd + (r + 64) * K);
+    const int64_t r = o0 + 128 * wave;
+    wsb[0] = reinterpret_cast<const uint8_t*>(wd + r * K);
+    wsb[1] = reinterpret_cast<const uint8_t*>(wd + (r + 64) * K);
   }
-  const int64_t rstride8 = static_cast<int64_t>(8) * K * 2;   // 8 weight rows, bytes
+  uint32_t woff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) woff[i] = static_cast<uint32_t>((8 * i + drow) * K * 2 + dch[i & 1] * 16);
   // ---- grouped rows of this wave's 4 DMA instructions (LDS rows 32w + 8i + drow) ----
-  const uint8_t* xb[4];
+  // contiguous rows (shared rows, ungathered routed rows, h) are offsets from
+  // the tile's first row; gathered rows are offsets token * H * 2 from x
+  // (under 2^32 bytes: tile_shapes_ok)
+  const bool gather = MODE == 0 && !sh && a.xr_rows != nullptr;
+  const int ld = MODE == 0 ? a.H : Fg;                          // row length, elements
+  const int64_t row0 = sh ? tl.row0 - TK : tl.row0;
+  const uint16_t* xbase = MODE == 0 ? static_cast<const uint16_t*>(sh ? a.xs : a.xr)
+                                    : static_cast<const uint16_t*>(sh ? a.h_sh : a.h);
+  const uint8_t* xsb = reinterpret_cast<const uint8_t*>(gather ? xbase : xbase + row0 * ld);
+  uint32_t xoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int tr = 32 * wave + 8 * i + drow;
-    const int64_t p = tl.row0 + min(tr, tl.rows - 1);
-    const uint16_t* base;
-    if (MODE == 0) {
-      if (sh) base = static_cast<const uint16_t*>(a.xs) + (p - TK) * a.H;
-      else base = static_cast<const uint16_t*>(a.xr) + (a.xr_rows ? a.xr_rows[p] : p) * a.H;
-    } else {
-      base = sh ? static_cast<const uint16_t*>(a.h_sh) + (p - TK) * a.Fs
-                : static_cast<const uint16_t*>(a.h) + p * a.F;
-    }
-    xb[i] = reinterpret_cast<const uint8_t*>(base) + dch[i & 1] * 16;
+    const int tr = min(32 * wave + 8 * i + drow, tl.rows - 1);
+    const int64_t r = gather ? a.xr_rows[tl.row0 + tr] : tr;
+    xoff[i] = static_cast<uint32_t>(r) * static_cast<uint32_t>(ld * 2) + dch[i & 1] * 16;
   }
 
   // DMA instruction g (0..19) of step s into stage st: 0-15 weight rows
   // (8 groups of 8 rows x 2 halves), 16-19 grouped rows
   auto dma = [&](int g, int s, uint8_t* st) {
-    const int64_t ko = static_cast<int64_t>(s) * kRowB;
+    const uint32_t ko = static_cast<uint32_t>(s) * kRowB;
     if (g < 16) {
       const int i = g >> 1, hf = g & 1;
-      dma16(wb[hf] + i * rstride8 + ko + dch[i & 1] * 16, st + (128 * wave + 64 * hf + 8 * i) * kRowB);
+      dma16(wsb[hf] + (woff[i] + ko), st + (128 * wave + 64 * hf + 8 * i) * kRowB);
     } else {
       const int i = g - 16;
-      dma16(xb[i] + ko, st + (kBW + 32 * wave + 8 * i) * kRowB);
+      dma16(xsb + (xoff[i] + ko), st + (kBW + 32 * wave + 8 * i) * kRowB);
     }
   };
 
@@ -177,27 +186,24 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
     for (int i = 0; i < 4; ++i) {
       const int c = i & 1;
       if (i < 3) frag(rd, i + 1, af[c ^ 1], bf[c ^ 1]);
-      if (i < 3) {
+      // the next step's 20 DMA issues: 10 in each of the first two sub-steps
+      const int d0 = i == 0 ? 0 : i == 1 ? 10 : 20;
+      const int d1 = i == 0 ? 10 : 20;
 #pragma unroll
-        for (int g = 0; g < 7; ++g)
-          if (7 * i + g < 20) dma(7 * i + g, sn, wr);
-      }
+      for (int g = d0; g < d1; ++g) dma(g, sn, wr);
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[m][n] = mma32(af[c][m], bf[c][n], acc[m][n]);
-      // 16 MFMAs; in between the next fragments' 8 LDS reads, then the DMAs
-      if (i < 3) {
+      const int nd = d1 - d0, nr = i < 3 ? 8 : 0;
+      // per MFMA: one fragment read (first 8), then this sub-step's DMAs spread
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        const int nd = i < 2 ? 7 : 6;
-        for (int g = 0; g < nd; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (g < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        const int k0 = g * nd / 16, k1 = (g + 1) * nd / 16;
+#pragma unroll
+        for (int q = k0; q < k1; ++q) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -331,9 +337,10 @@ int tile_ksplit(int64_t blocks, int K1, int K2, int max_ks, int target) {
   return ks;
 }
 
-// slabs must divide the weight dimensions: F, Fs by 256, H by 512
-bool tile_shapes_ok(int H, int F, int Fs) {
-  return F % (kBW / 2) == 0 && Fs % (kBW / 2) == 0 && H % kBW == 0;
+// slabs must divide the weight dimensions: F, Fs by 256, H by 512; the
+// token-row DMA offsets (token * H * 2 bytes) must fit in 32 bits
+bool tile_shapes_ok(int64_t T, int H, int F, int Fs) {
+  return F % (kBW / 2) == 0 && Fs % (kBW / 2) == 0 && H % kBW == 0 && T * H * 2 <= 0xffffffffLL;
 }
 
 template <int MODE>

@@ -113,7 +113,7 @@ struct FfnPlan {
   }
 };
 FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype);
-bool tile_shapes_ok(int H, int F, int Fs);
+bool tile_shapes_ok(int64_t T, int H, int F, int Fs);
 // per-kernel-family launchers (ffn_stream.hip, ffn_fp8.hip)
 hipError_t launch_gate_up_stream(const FfnArgs& a, hipStream_t st);
 hipError_t launch_down_stream(const FfnArgs& a, hipStream_t st);
