@@ -35,6 +35,8 @@
 // (slab, tile) pairs are numbered slab-major and cut into 8 contiguous
 // ranges, range i going to the blocks that land on XCD i, so the tiles that
 // share a weight slab run on one XCD and reuse its L2, for any slab count.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace moe {
@@ -156,132 +158,147 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
     }
   };
 
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
-
   // this block's K steps [s0, s0 + steps); steps is even
   const int steps = K / kBK / ks, s0 = kp * steps;
   const int sw = (r32 >> 1) & 7;                       // row swizzle of this lane's rows
   const int arow = (128 * wave + r32) * kRowB;
   const int brow = (kBW + r32) * kRowB;
-  // fragments of sub-step i (16 K-elements) of a step from stage st
-  auto frag = [&](const uint8_t* st, int i, uint4 (&af)[4], uint4 (&bf)[4]) {
-    const int slot = ((kh * 4 + i) ^ sw) * 16;
+
+  // The K loop and the epilogue for NN active 32-row groups of grouped rows
+  // (NN = ceil(rows / 32)): a work list's last tile of an expert is usually
+  // partly filled, and its MFMAs and fragment reads on groups past the last
+  // row are skipped (block-uniform: every wave covers all the tile's rows).
+  auto run = [&](auto nn_tag) {
+    constexpr int NN = decltype(nn_tag)::value;
+    f32x16 acc[4][NN];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) af[m] = *reinterpret_cast<const uint4*>(st + arow + 32 * m * kRowB + slot);
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) bf[n] = *reinterpret_cast<const uint4*>(st + brow + 32 * n * kRowB + slot);
-  };
-  // one K step: MFMAs on stage rd while the DMA of step sn fills stage wr;
-  // the next sub-step's fragments are read during the current sub-step
-  auto step = [&](const uint8_t* rd, uint8_t* wr, int sn) {
-    uint4 af[2][4], bf[2][4];
-    frag(rd, 0, af[0], bf[0]);
+      for (int n = 0; n < NN; ++n)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = i & 1;
-      if (i < 3) frag(rd, i + 1, af[c ^ 1], bf[c ^ 1]);
-      // the next step's 20 DMA issues: 10 in each of the first two sub-steps
-      const int d0 = i == 0 ? 0 : i == 1 ? 10 : 20;
-      const int d1 = i == 0 ? 10 : 20;
+        for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
+
+    // fragments of sub-step i (16 K-elements) of a step from stage st
+    auto frag = [&](const uint8_t* st, int i, uint4 (&af)[4], uint4 (&bf)[NN]) {
+      const int slot = ((kh * 4 + i) ^ sw) * 16;
 #pragma unroll
-      for (int g = d0; g < d1; ++g) dma(g, sn, wr);
+      for (int m = 0; m < 4; ++m) af[m] = *reinterpret_cast<const uint4*>(st + arow + 32 * m * kRowB + slot);
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int n = 0; n < NN; ++n) bf[n] = *reinterpret_cast<const uint4*>(st + brow + 32 * n * kRowB + slot);
+    };
+    // one K step: MFMAs on stage rd while the DMA of step sn fills stage wr;
+    // the next sub-step's fragments are read during the current sub-step
+    auto step = [&](const uint8_t* rd, uint8_t* wr, int sn) {
+      uint4 af[2][4], bf[2][NN];
+      frag(rd, 0, af[0], bf[0]);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = mma32(af[c][m], bf[c][n], acc[m][n]);
-      const int nd = d1 - d0, nr = i < 3 ? 8 : 0;
-      // per MFMA: one fragment read (first 8), then this sub-step's DMAs spread
+      for (int i = 0; i < 4; ++i) {
+        const int c = i & 1;
+        if (i < 3) frag(rd, i + 1, af[c ^ 1], bf[c ^ 1]);
+        // the next step's 20 DMA issues: 10 in each of the first two sub-steps
+        const int d0 = i == 0 ? 0 : i == 1 ? 10 : 20;
+        const int d1 = i == 0 ? 10 : 20;
 #pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (g < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        const int k0 = g * nd / 16, k1 = (g + 1) * nd / 16;
+        for (int g = d0; g < d1; ++g) dma(g, sn, wr);
 #pragma unroll
-        for (int q = k0; q < k1; ++q) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int n = 0; n < NN; ++n) acc[m][n] = mma32(af[c][m], bf[c][n], acc[m][n]);
+        // among its MFMAs: the next fragments' LDS reads as early as
+        // possible, this sub-step's DMAs spread evenly
+        constexpr int nm = 4 * NN;
+        const int nd = d1 - d0, nr = i < 3 ? 4 + NN : 0, rp = (nr + nm - 1) / nm;
+#pragma unroll
+        for (int g = 0; g < nm; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+          for (int q = g * rp; q < min((g + 1) * rp, nr); ++q) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+          for (int q = g * nd / nm; q < (g + 1) * nd / nm; ++q) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    };
+
+#pragma unroll
+    for (int g = 0; g < 20; ++g) dma(g, s0, st0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-  };
+    for (int s = 0; s < steps; s += 2) {
+      step(st0, st1, s0 + s + 1);
+      step(st1, st0, s0 + min(s + 2, steps - 1));
+    }
+    if (ks > 1) {
+      // ---- partial sums: row p of part kp holds gate | up (gate_up, width
+      // 2 * max(F, Fs)) or the output row (down, width H), fp32 ----
+      const int64_t R = TK + a.T;
+      const int width = MODE == 0 ? 2 * max(a.F, a.Fs) : a.H;
+  #pragma unroll
+      for (int n = 0; n < NN; ++n) {
+        const int tr = 32 * n + r32;
+        if (tr >= tl.rows) continue;
+        float* dst = a.part + (static_cast<int64_t>(kp) * R + tl.row0 + tr) * width;
+  #pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          // gate_up: m = 0, 1 gate features, 2, 3 the same features' up rows
+          const int col = MODE == 0 ? (m >> 1) * (width / 2) + o0 + 64 * wave + 32 * (m & 1)
+                                    : o0 + 128 * wave + 32 * m;
+  #pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(dst + col + 8 * g + 4 * kh) =
+                make_float4(acc[m][n][4 * g], acc[m][n][4 * g + 1], acc[m][n][4 * g + 2], acc[m][n][4 * g + 3]);
+        }
+      }
+      return;
+    }
 
-#pragma unroll
-  for (int g = 0; g < 20; ++g) dma(g, s0, st0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int s = 0; s < steps; s += 2) {
-    step(st0, st1, s0 + s + 1);
-    step(st1, st0, s0 + min(s + 2, steps - 1));
-  }
-
-  if (ks > 1) {
-    // ---- partial sums: row p of part kp holds gate | up (gate_up, width
-    // 2 * max(F, Fs)) or the output row (down, width H), fp32 ----
-    const int64_t R = TK + a.T;
-    const int width = MODE == 0 ? 2 * max(a.F, a.Fs) : a.H;
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    // ---- epilogue: lane holds rows 8*(i/4) + 4*kh + (i%4) of each 32-row
+    // weight sub-tile, for grouped row 32*n + r32 ----
+  #pragma unroll
+    for (int n = 0; n < NN; ++n) {
       const int tr = 32 * n + r32;
       if (tr >= tl.rows) continue;
-      float* dst = a.part + (static_cast<int64_t>(kp) * R + tl.row0 + tr) * width;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        // gate_up: m = 0, 1 gate features, 2, 3 the same features' up rows
-        const int col = MODE == 0 ? (m >> 1) * (width / 2) + o0 + 64 * wave + 32 * (m & 1)
-                                  : o0 + 128 * wave + 32 * m;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<float4*>(dst + col + 8 * g + 4 * kh) =
-              make_float4(acc[m][n][4 * g], acc[m][n][4 * g + 1], acc[m][n][4 * g + 2], acc[m][n][4 * g + 3]);
+      const int64_t p = tl.row0 + tr;
+      if (MODE == 0) {
+        uint16_t* dst = sh ? static_cast<uint16_t*>(a.h_sh) + (p - TK) * a.Fs
+                           : static_cast<uint16_t*>(a.h) + p * a.F;
+        dst += o0 + 64 * wave + 4 * kh;
+  #pragma unroll
+        for (int m = 0; m < 2; ++m)
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float h[4];
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = silu(acc[m][n][4 * g + e]) * acc[m + 2][n][4 * g + e];
+            uint2 v2;
+            v2.x = pack_bf16(h[0], h[1]);
+            v2.y = pack_bf16(h[2], h[3]);
+            *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g) = v2;
+          }
+      } else {
+        uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (p - TK) * a.H
+                           : static_cast<uint16_t*>(a.y) + p * a.H;
+        dst += o0 + 128 * wave + 4 * kh;
+  #pragma unroll
+        for (int m = 0; m < 4; ++m)
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint2 v2;
+            v2.x = pack_bf16(acc[m][n][4 * g + 0], acc[m][n][4 * g + 1]);
+            v2.y = pack_bf16(acc[m][n][4 * g + 2], acc[m][n][4 * g + 3]);
+            *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g) = v2;
+          }
       }
     }
-    return;
-  }
+  };
 
-  // ---- epilogue: lane holds rows 8*(i/4) + 4*kh + (i%4) of each 32-row
-  // weight sub-tile, for grouped row 32*n + r32 ----
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int tr = 32 * n + r32;
-    if (tr >= tl.rows) continue;
-    const int64_t p = tl.row0 + tr;
-    if (MODE == 0) {
-      uint16_t* dst = sh ? static_cast<uint16_t*>(a.h_sh) + (p - TK) * a.Fs
-                         : static_cast<uint16_t*>(a.h) + p * a.F;
-      dst += o0 + 64 * wave + 4 * kh;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float h[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = silu(acc[m][n][4 * g + e]) * acc[m + 2][n][4 * g + e];
-          uint2 v2;
-          v2.x = pack_bf16(h[0], h[1]);
-          v2.y = pack_bf16(h[2], h[3]);
-          *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g) = v2;
-        }
-    } else {
-      uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (p - TK) * a.H
-                         : static_cast<uint16_t*>(a.y) + p * a.H;
-      dst += o0 + 128 * wave + 4 * kh;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 v2;
-          v2.x = pack_bf16(acc[m][n][4 * g + 0], acc[m][n][4 * g + 1]);
-          v2.y = pack_bf16(acc[m][n][4 * g + 2], acc[m][n][4 * g + 3]);
-          *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g) = v2;
-        }
-    }
-  }
+  const int nn = (tl.rows + 31) >> 5;
+  if (nn >= 4) run(std::integral_constant<int, 4>{});
+  else if (nn == 3) run(std::integral_constant<int, 3>{});
+  else if (nn == 2) run(std::integral_constant<int, 2>{});
+  else run(std::integral_constant<int, 1>{});
 }
 
 // Sum of the K-part partials of each grouped row in part order, then the
