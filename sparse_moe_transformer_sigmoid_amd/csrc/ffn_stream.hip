@@ -327,8 +327,8 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
     // expected work items with the rows spread evenly over the experts
     const int64_t per_e = (rows + a.E - 1) / a.E;
     const int64_t items = a.E * ((per_e + 127) / 128) + (a.Fs > 0 ? (a.T + 127) / 128 : 0);
-    p.ks_gu = tile_ksplit(items * (std::max(a.F, a.Fs) / 256), a.H, a.H, 8, 256);
-    p.ks_dn = tile_ksplit(items * (a.H / 512), a.F, a.Fs > 0 ? a.Fs : a.F, 16, 128);
+    p.ks_gu = tile_ksplit(items * (std::max(a.F, a.Fs) / 256), a.H, a.H, 8, 256, true);
+    p.ks_dn = tile_ksplit(items * (a.H / 512), a.F, a.Fs > 0 ? a.Fs : a.F, 16, 128, false);
     return p;
   }
   const int bm = per_expert < 6.0 ? 16 : (per_expert < 12.0 ? 32 : 64);

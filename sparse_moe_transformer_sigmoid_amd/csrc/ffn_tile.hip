@@ -345,12 +345,20 @@ int tile_rows() { return kBM; }
 // K parts of the tiled kernels for a grid of `blocks` (slabs x work items):
 // doubled (up to max_ks) while the grid has fewer than `target` blocks (the
 // kernel holds a whole CU's LDS, so 256 blocks fill the chip), keeping every
-// part an even number of 64-wide steps of both K1 and K2.  Measured: gate_up
-// gains up to 256 blocks; down, whose partial sums are 7168 wide, only below
-// 128 (at 140 blocks the extra pass cost more than the split gained).
-int tile_ksplit(int64_t blocks, int K1, int K2, int max_ks, int target) {
+// part an even number of 64-wide steps of both K1 and K2.  With `one_round`
+// the doubled grid must still fit in `target` blocks: a grid just past one
+// round of the chip runs two rounds of half-length blocks plus twice the
+// partial sums.  Measured on MI355X: gate_up (one_round, 256): 72 blocks
+// (one expert-parallel rank's 3 experts, the dense layer's one) take 0.142 /
+// 0.166 ms with 2 parts against 0.158 / 0.195 ms with 4; down (128, fp32
+// partial sums 7168 wide): the dense layer's 14 blocks gain up to 16 parts
+// (0.10 ms against 0.154 with 4), while at 140 blocks the extra pass cost
+// more than the split gained.
+int tile_ksplit(int64_t blocks, int K1, int K2, int max_ks, int target, bool one_round) {
   int ks = 1;
-  while (ks < max_ks && blocks * ks < target && (K1 / kBK) % (4 * ks) == 0 && (K2 / kBK) % (4 * ks) == 0) ks *= 2;
+  while (ks < max_ks && blocks * (one_round ? 2 * ks : ks) <= (one_round ? target : target - 1) &&
+         (K1 / kBK) % (4 * ks) == 0 && (K2 / kBK) % (4 * ks) == 0)
+    ks *= 2;
   return ks;
 }
 

@@ -124,7 +124,7 @@ int fp8_tile_rows();
 hipError_t launch_gate_up_tile(const FfnArgs& a, hipStream_t st);  // ffn_tile.hip
 hipError_t launch_down_tile(const FfnArgs& a, hipStream_t st);
 int tile_rows();
-int tile_ksplit(int64_t blocks, int K1, int K2, int max_ks, int target);
+int tile_ksplit(int64_t blocks, int K1, int K2, int max_ks, int target, bool one_round);
 
 // pre-MoE RMSNorm, fp64, rounded once to the activation dtype into u [T][H];
 // with `codes` (bf16 only) also the fp8 quantisation of u (codes [T][H],
