@@ -34,7 +34,8 @@ SMALL = [
     # size 384 (not a multiple of the 256-row slab) at 100 tokens: streamed
     # items of 64 rows
     (W["small_bf16"], 1), (W["small_bf16"], 7), (W["small_bf16"], 28), (W["small_bf16"], 40),
-    (W["small_bf16"], 100), (W["small_bf16"], 300), (W["small_bf16"], 1024), (W["small_bf16"], 4096),
+    (W["small_bf16"], 100), (W["small_bf16"], 256), (W["small_bf16"], 257), (W["small_bf16"], 300),
+    (W["small_bf16"], 1024), (W["small_bf16"], 4096),
     (W["small_bf16"].replace(name="small_bf16_f384", moe_intermediate_size=384), 100),
     (W["small_bf16"].replace(name="small_bf16_e64", n_routed_experts=64), 1100),
     (W["small_grouped_bf16"], 100),
@@ -71,10 +72,15 @@ def check_fp8_codes(x: torch.Tensor, sorted_ids: np.ndarray, codes: torch.Tensor
     assert len(bad) == 0, f"{len(bad)} activation codes differ, first {bad[:3].tolist()}"
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "small_bf16", "small_grouped_bf16", "small_fp8"])
-def test_stages_match_oracle_and_layer(name):
+# up to 256 tokens the grouping (and, in the layer, the work list) is one
+# single-block kernel; from 257 on, per-chunk histograms, a scan and a
+# scatter over 256-token chunks (1024: four chunks)
+@pytest.mark.parametrize("name,T", [("tiny_fp32", 16), ("small_bf16", 100), ("small_grouped_bf16", 100),
+                                    ("small_fp8", 100), ("small_bf16", 256), ("small_bf16", 257),
+                                    ("small_bf16", 1024), ("small_fp8", 257)])
+def test_stages_match_oracle_and_layer(name, T):
     wl = W[name]
-    case = small_case(wl, wl.num_tokens)
+    case = small_case(wl, T)
     r = run_stages(wl, case)
     ref, route = cases.oracle_forward(wl, case)
     check_route(r["ids"], r["w"], route)
