@@ -333,8 +333,9 @@ def main():
                     help="comma-separated token counts measured after the main line (stderr / --extra-out)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
-              "(the layer runs unsharded on a single MI355X)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer runs unsharded on a single MI355X)",
+              file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

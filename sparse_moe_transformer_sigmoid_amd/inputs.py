@@ -121,7 +121,9 @@ def _k2(name, T, **kw) -> Workload:
     return Workload(name=name, num_tokens=T, **base)
 
 
-# The five workloads of the benchmark spec, plus small parity shapes.
+# The Kimi-K2 layer workloads (decode, Zipf prefill, fp8, the DeepSeek-V3 and
+# Moonlight shapes, the sub-block, the dense layer, expert-parallel rank
+# shares), plus small parity shapes.
 WORKLOADS: Dict[str, Workload] = {
     "tiny_fp32": Workload("tiny_fp32", 16, 256, 128, 16, 4, act_dtype=F32, weight_dtype=F32),
     "k2_decode_bf16": _k2("k2_decode_bf16", 128),

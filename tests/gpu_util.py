@@ -1,5 +1,6 @@
 """Helpers of the GPU tests: run the HIP path through the C ABI and compare
-with the oracle at the benchmark's tolerances."""
+with the oracle at the stated tolerances (TOL: relative error of the layer
+output per weight dtype; W_RTOL: routing weights)."""
 from __future__ import annotations
 
 import sys
