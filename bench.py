@@ -122,14 +122,16 @@ def source_hash(name: str) -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16] if os.path.exists(p) else ""
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, num_tokens: int):
     """HBM bytes per gate_up launch measured by rocprofv3 counters (FETCH_SIZE +
-    WRITE_SIZE scaled by a 1 GiB copy), if they were taken on the current
-    sources of that kernel (else None)."""
+    WRITE_SIZE scaled by a 1 GiB copy), if they were taken for this token
+    count on the current sources of that kernel (else None)."""
     p = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
+    if d.get("num_tokens") != num_tokens:
+        return None
     if any(source_hash(f) != h for f, h in d.get("sources", {}).items()):
         return None
     return d.get("traffic_bytes")
@@ -392,7 +394,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    rl = roofline(wl, T, n_active, gate_up_ms, stored_traffic(args.workload), routed_rows)
+    rl = roofline(wl, T, n_active, gate_up_ms, stored_traffic(args.workload, T), routed_rows)
     res = {
         "metric": METRIC, "value": round(T * args.steps / wall, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),

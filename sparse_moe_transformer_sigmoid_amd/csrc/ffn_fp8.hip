@@ -9,10 +9,14 @@
 //    one 128-wide K block, so each partial product is rescaled once by the
 //    weight block scale times the token's activation scale before it joins
 //    the fp32 accumulator: acc += (sum_k qw qa) * s_w * s_a;
-//  * a work item covers up to 64 grouped rows (4 sub-tiles of 16) so that an
-//    expert with tens of rows streams its weights once per 64 rows; all four
-//    sub-tiles are computed (rows past the tile repeat its last row and are
-//    not stored), which keeps the loop free of divergent control flow.
+//  * a work item covers up to 16 * NT grouped rows (NT = 1, 2, 4 sub-tiles of
+//    16, chosen from the rows per expert) so that an expert with tens of rows
+//    streams its weights once per item; all NT sub-tiles are computed (rows
+//    past the tile repeat its last row and are not stored), which keeps the
+//    loop free of divergent control flow.
+// Each wave's loads for its next K step (operands and scales) are issued
+// before the current step's MFMAs, so a load's latency overlaps a step of
+// compute instead of stalling every step.
 // The SwiGLU output is written in fp32; the activation-quant kernel turns it
 // into e4m3 codes + per-128 scales for the down projection.
 #include "kernels.h"
@@ -22,7 +26,6 @@ namespace moe {
 namespace {
 
 constexpr int kWK = 4;   // waves splitting K
-constexpr int kNT = 4;   // 16-row sub-tiles per work item
 
 __device__ __forceinline__ f32x4 mma_fp8(const uint4 (&a)[2], const uint4 (&b)[2]) {
   i32x8 av, bv;
@@ -35,58 +38,84 @@ __device__ __forceinline__ f32x4 mma_fp8(const uint4 (&a)[2], const uint4 (&b)[2
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 0, 0, 0, 127, 0, 127);
 }
 
-__device__ __forceinline__ void load32(uint4 (&d)[2], const uint8_t* p) {
-  const uint4* s = reinterpret_cast<const uint4*>(p);
-  d[0] = s[0];
-  d[1] = s[1];
+// One wave's operands of one K step (one 128-wide quantisation block): 32
+// bytes per lane of NA weight row-tiles and NT token sub-tiles, and their
+// scales.
+template <int NA, int NT>
+struct Frag8 {
+  uint4 a[NA][2];
+  uint4 b[NT][2];
+  float ws[NA];
+  float bs[NT];
+};
+
+template <int NA, int NT>
+__device__ __forceinline__ void load_frag8(Frag8<NA, NT>& f, const uint8_t* const (&pa)[NA],
+                                           const float* const (&wsc)[NA],
+                                           const uint8_t* const (&pb)[NT],
+                                           const float* const (&bsc)[NT], int s) {
+  const int koff = s * 128;
+#pragma unroll
+  for (int m = 0; m < NA; ++m) {
+    const uint4* p = reinterpret_cast<const uint4*>(pa[m] + koff);
+    f.a[m][0] = p[0];
+    f.a[m][1] = p[1];
+    f.ws[m] = wsc[m][s];
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const uint4* p = reinterpret_cast<const uint4*>(pb[n] + koff);
+    f.b[n][0] = p[0];
+    f.b[n][1] = p[1];
+    f.bs[n] = bsc[n][s];
+  }
 }
 
-// One wave's K loop for NA weight row-tiles of 16 rows and up to kNT token
-// sub-tiles; then the kWK partial sums are added in LDS (wave 0 keeps them).
-template <int NA>
+template <int NA, int NT>
+__device__ __forceinline__ void mma_frag8(const Frag8<NA, NT>& f, f32x4 (&acc)[NA][NT]) {
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int m = 0; m < NA; ++m) {
+      const f32x4 c = mma_fp8(f.a[m], f.b[n]);
+      const float sc = f.ws[m] * f.bs[n];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(c[i], sc, acc[m][n][i]);
+    }
+}
+
+// One wave's K loop for NA weight row-tiles of 16 rows and NT token
+// sub-tiles (steps wave, wave + kWK, ..., the next step's loads in flight
+// during the current step's MFMAs); then the kWK partial sums are added in
+// LDS in wave order (wave 0 keeps them).
+template <int NA, int NT>
 __device__ __forceinline__ void stream_k_fp8(const uint8_t* const (&pa)[NA],
                                              const float* const (&wsc)[NA],
-                                             const uint8_t* const (&pb)[kNT],
-                                             const float* const (&bsc)[kNT], int steps,
-                                             f32x4 (&acc)[NA][kNT]) {
-  __shared__ f32x4 red[kWK - 1][NA][kNT][64];
+                                             const uint8_t* const (&pb)[NT],
+                                             const float* const (&bsc)[NT], int steps,
+                                             f32x4 (&acc)[NA][NT]) {
+  __shared__ f32x4 red[kWK - 1][NA][NT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int m = 0; m < NA; ++m)
 #pragma unroll
-    for (int n = 0; n < kNT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int s = wave;
+  Frag8<NA, NT> cur, nxt;
+  if (s < steps) load_frag8(cur, pa, wsc, pb, bsc, s);
 #pragma unroll 1
-  for (int s = wave; s < steps; s += kWK) {
-    const int koff = s * 128;
-    uint4 a[NA][2], b[kNT][2];
-    float ws[NA], bs[kNT];
-#pragma unroll
-    for (int m = 0; m < NA; ++m) {
-      load32(a[m], pa[m] + koff);
-      ws[m] = wsc[m][s];
-    }
-    // sub-tiles past the tile's rows point at its last valid row, so every
-    // load is in bounds
-#pragma unroll
-    for (int n = 0; n < kNT; ++n) {
-      load32(b[n], pb[n] + koff);
-      bs[n] = bsc[n][s];
-    }
-#pragma unroll
-    for (int n = 0; n < kNT; ++n)
-#pragma unroll
-      for (int m = 0; m < NA; ++m) {
-          const f32x4 c = mma_fp8(a[m], b[n]);
-          const float sc = ws[m] * bs[n];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(c[i], sc, acc[m][n][i]);
-      }
+  while (s < steps) {
+    const int sn = s + kWK;
+    if (sn < steps) load_frag8(nxt, pa, wsc, pb, bsc, sn);
+    mma_frag8(cur, acc);
+    cur = nxt;
+    s = sn;
   }
   if (wave > 0)
 #pragma unroll
     for (int m = 0; m < NA; ++m)
 #pragma unroll
-      for (int n = 0; n < kNT; ++n) red[wave - 1][m][n][lane] = acc[m][n];
+      for (int n = 0; n < NT; ++n) red[wave - 1][m][n][lane] = acc[m][n];
   __syncthreads();
   if (wave == 0)
 #pragma unroll
@@ -94,13 +123,14 @@ __device__ __forceinline__ void stream_k_fp8(const uint8_t* const (&pa)[NA],
 #pragma unroll
       for (int m = 0; m < NA; ++m)
 #pragma unroll
-        for (int n = 0; n < kNT; ++n) acc[m][n] += red[w][m][n][lane];
+        for (int n = 0; n < NT; ++n) acc[m][n] += red[w][m][n][lane];
 }
 
 }  // namespace
 
 // gate_up: block = 16 intermediate features (16 gate + 16 up weight rows) of
-// one work item (<= 64 grouped rows); h written in fp32.
+// one work item (<= 16 * NT grouped rows); h written in fp32.
+template <int NT>
 __global__ __launch_bounds__(256) void gate_up_stream_fp8(FfnArgs a) {
   const int ti = blockIdx.y;
   if (ti >= *a.tile_count) return;
@@ -119,10 +149,10 @@ __global__ __launch_bounds__(256) void gate_up_stream_fp8(FfnArgs a) {
   const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.F / 128) * KB) + (f0 / 128) * KB;
   const uint8_t* pa[2] = {wg + wofs + (f0 + r) * H + q * 32, wu + wofs + (f0 + r) * H + q * 32};
   const float* wsc[2] = {sg + sofs, su + sofs};
-  const uint8_t* pb[kNT];
-  const float* bsc[kNT];
+  const uint8_t* pb[NT];
+  const float* bsc[NT];
 #pragma unroll
-  for (int n = 0; n < kNT; ++n) {
+  for (int n = 0; n < NT; ++n) {
     const int64_t p = tl.row0 + min(n * 16 + r, tl.rows - 1);
     int64_t row;
     const uint8_t* base;
@@ -139,11 +169,11 @@ __global__ __launch_bounds__(256) void gate_up_stream_fp8(FfnArgs a) {
     pb[n] = base + row * H + q * 32;
     bsc[n] = sbase + row * KB;
   }
-  f32x4 acc[2][kNT];
+  f32x4 acc[2][NT];
   stream_k_fp8<2>(pa, wsc, pb, bsc, static_cast<int>(KB), acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
-  for (int n = 0; n < kNT; ++n) {
+  for (int n = 0; n < NT; ++n) {
     if (n * 16 + r >= tl.rows) continue;
     const int64_t pr = tl.row0 + n * 16 + r;
     float* dst = sh ? static_cast<float*>(a.h_sh) + (pr - TK) * a.Fs : static_cast<float*>(a.h) + pr * a.F;
@@ -157,6 +187,7 @@ __global__ __launch_bounds__(256) void gate_up_stream_fp8(FfnArgs a) {
 }
 
 // down: block = 32 hidden outputs of one work item; input = quantised h
+template <int NT>
 __global__ __launch_bounds__(256) void down_stream_fp8(FfnArgs a) {
   const int ti = blockIdx.y;
   if (ti >= *a.tile_count) return;
@@ -173,10 +204,10 @@ __global__ __launch_bounds__(256) void down_stream_fp8(FfnArgs a) {
   const uint8_t* pa[2] = {wd + wofs + static_cast<int64_t>(h0 + r) * Fg + q * 32,
                           wd + wofs + static_cast<int64_t>(h0 + 16 + r) * Fg + q * 32};
   const float* wsc[2] = {sd + sofs, sd + sofs};
-  const uint8_t* pb[kNT];
-  const float* bsc[kNT];
+  const uint8_t* pb[NT];
+  const float* bsc[NT];
 #pragma unroll
-  for (int n = 0; n < kNT; ++n) {
+  for (int n = 0; n < NT; ++n) {
     const int64_t p = tl.row0 + min(n * 16 + r, tl.rows - 1);
     if (sh) {
       pb[n] = static_cast<const uint8_t*>(a.hq_sh) + (p - TK) * a.Fs + q * 32;
@@ -186,11 +217,11 @@ __global__ __launch_bounds__(256) void down_stream_fp8(FfnArgs a) {
       bsc[n] = a.h_scales + p * KB;
     }
   }
-  f32x4 acc[2][kNT];
+  f32x4 acc[2][NT];
   stream_k_fp8<2>(pa, wsc, pb, bsc, static_cast<int>(KB), acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
-  for (int n = 0; n < kNT; ++n) {
+  for (int n = 0; n < NT; ++n) {
     if (n * 16 + r >= tl.rows) continue;
     const int64_t pr = tl.row0 + n * 16 + r;
     uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (pr - TK) * a.H : static_cast<uint16_t*>(a.y) + pr * a.H;
@@ -204,11 +235,14 @@ __global__ __launch_bounds__(256) void down_stream_fp8(FfnArgs a) {
   }
 }
 
-int fp8_tile_rows() { return 16 * kNT; }
-
 hipError_t launch_gate_up_fp8(const FfnArgs& a, hipStream_t st) {
   dim3 grid(std::max(a.F, a.Fs) / 16, static_cast<unsigned>(a.tile_bound));
-  hipLaunchKernelGGL(gate_up_stream_fp8, grid, dim3(256), 0, st, a);
+  switch (a.bm) {
+    case 16: hipLaunchKernelGGL(gate_up_stream_fp8<1>, grid, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(gate_up_stream_fp8<2>, grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(gate_up_stream_fp8<4>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // SwiGLU output -> e4m3 codes + per-128 scales for the down projection
@@ -221,7 +255,12 @@ hipError_t launch_gate_up_fp8(const FfnArgs& a, hipStream_t st) {
 
 hipError_t launch_down_fp8(const FfnArgs& a, hipStream_t st) {
   dim3 grid(a.H / 32, static_cast<unsigned>(a.tile_bound));
-  hipLaunchKernelGGL(down_stream_fp8, grid, dim3(256), 0, st, a);
+  switch (a.bm) {
+    case 16: hipLaunchKernelGGL(down_stream_fp8<1>, grid, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(down_stream_fp8<2>, grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(down_stream_fp8<4>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

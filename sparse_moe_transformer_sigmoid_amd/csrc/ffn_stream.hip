@@ -312,14 +312,18 @@ namespace moe {
 //    kernels with work items of 16 rows below 6 rows per expert, 32 below 12
 //    and 64 beyond (128-row items run at half occupancy and were slower in
 //    every case);
-//  * fp8: the fp8 tiled kernel from r = 32 on, else its streaming kernel.
+//  * fp8: the fp8 tiled kernel from r = 8 on as well (K2 fp8 layer, whole
+//    layer, tiled vs streamed: T=384, r=8: 3.10 vs 3.30 ms; T=512: 3.21 vs
+//    3.63; T=1024: 3.43 vs 5.28), else its streaming kernel with the same
+//    16 / 32 / 64-row work items.
 FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   if (act_dtype == MOE_F32) return {16, FfnPlan::kSimple};
   const int64_t rows = static_cast<int64_t>(a.T) * a.k;
   const double per_expert = static_cast<double>(rows) / a.E;
+  const int stream_bm = per_expert < 6.0 ? 16 : (per_expert < 12.0 ? 32 : 64);
   if (weight_dtype == MOE_FP8_E4M3)
-    return per_expert >= 32.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? FfnPlan{tile_fp8_rows(), FfnPlan::kTiled}
-                                                                   : FfnPlan{fp8_tile_rows(), FfnPlan::kStream};
+    return per_expert >= 8.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? FfnPlan{tile_fp8_rows(), FfnPlan::kTiled}
+                                                                   : FfnPlan{stream_bm, FfnPlan::kStream};
   if (per_expert >= 8.0 && tile_shapes_ok(a.T, a.H, a.F, a.Fs)) {
     // few work items (few, fat experts: one expert-parallel rank, the dense
     // layer) split the K loop so that the grid still fills the chip
@@ -331,8 +335,7 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
     p.ks_dn = tile_ksplit(items * (a.H / 512), a.F, a.Fs > 0 ? a.Fs : a.F, 16, 128, false);
     return p;
   }
-  const int bm = per_expert < 6.0 ? 16 : (per_expert < 12.0 ? 32 : 64);
-  return {bm, FfnPlan::kStream};
+  return {stream_bm, FfnPlan::kStream};
 }
 
 hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {

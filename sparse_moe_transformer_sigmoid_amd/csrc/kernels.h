@@ -120,7 +120,6 @@ hipError_t launch_down_stream(const FfnArgs& a, hipStream_t st);
 hipError_t launch_simple_f32(const FfnArgs& a, bool gate_up, hipStream_t st);
 hipError_t launch_gate_up_fp8(const FfnArgs& a, hipStream_t st);
 hipError_t launch_down_fp8(const FfnArgs& a, hipStream_t st);
-int fp8_tile_rows();
 hipError_t launch_gate_up_tile(const FfnArgs& a, hipStream_t st);  // ffn_tile.hip
 hipError_t launch_down_tile(const FfnArgs& a, hipStream_t st);
 int tile_rows();
