@@ -8,6 +8,9 @@
 
 namespace moe {
 
+// K parts of the small-batch logits kernel (partial sums added by top-k)
+constexpr int kMaxParts = 8;
+
 // ---------------------------------------------------------------------------
 // logits, bf16: one block = 16 tokens x 16 experts, 4 waves split the K loop
 // (K steps of 128 taken round-robin), reduced through LDS in a fixed order.
@@ -32,16 +35,28 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const uint16_t* __rest
   const int steps = H / 128, per = (steps + gridDim.z - 1) / gridDim.z;
   const int s0 = blockIdx.z * per, s1 = min(s0 + per, steps);
   logits += static_cast<int64_t>(blockIdx.z) * T * E;
-  for (int s = s0 + wave; s < s1; s += 4) {
+  // steps s0 + wave, s0 + wave + 4, ...; the next step's loads are issued
+  // before the current step's MFMAs
+  auto load = [&](int s, uint4 (&a)[4], uint4 (&b)[4]) {
     const uint4* a4 = reinterpret_cast<const uint4*>(pa + s * 128);
     const uint4* b4 = reinterpret_cast<const uint4*>(pb + s * 128);
-    uint4 a[4], b[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) { a[i] = a4[i]; b[i] = b4[i]; }
+  };
+  uint4 a[4], b[4], an[4], bn[4];
+  int s = s0 + wave;
+  if (s < s1) load(s, a, b);
+#pragma unroll 1
+  while (s < s1) {
+    const int sn = s + 4;
+    if (sn < s1) load(sn, an, bn);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
                                                     __builtin_bit_cast(bf16x8, b[i]), acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = an[i]; b[i] = bn[i]; }
+    s = sn;
   }
   if (wave > 0) red[wave - 1][lane] = acc;
   __syncthreads();
@@ -164,13 +179,24 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
   const bool valid = t < T;
   const int tt = valid ? t : T - 1;
   float s[V], sel[V];
+  // partial logits of the K parts (at most kMaxParts), all loaded before
+  // they are added in part order
+  float zp[kMaxParts][V];
+#pragma unroll
+  for (int p = 0; p < kMaxParts; ++p)
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int e = lane * V + i;
+      zp[p][i] = p < kparts && e < E ? logits[(static_cast<int64_t>(p) * T + tt) * E + e] : 0.f;
+    }
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int e = lane * V + i;
     if (e < E) {
-      // partial logits of the K parts, added in part order
-      float z = logits[static_cast<int64_t>(tt) * E + e];
-      for (int p = 1; p < kparts; ++p) z += logits[(static_cast<int64_t>(p) * T + tt) * E + e];
+      float z = zp[0][i];
+#pragma unroll
+      for (int p = 1; p < kMaxParts; ++p)
+        if (p < kparts) z += zp[p][i];
       s[i] = 1.0f / (1.0f + expf(-z));
       sel[i] = s[i] + bias[e];
     } else {
@@ -257,7 +283,7 @@ int router_kparts(int64_t T, int E, int H, bool bf16) {
   if (!bf16 || (T >= 512 && E % 64 == 0)) return 1;
   const int64_t blocks = static_cast<int64_t>((E + 15) / 16) * ((T + 15) / 16);
   int kp = 1;
-  while (kp < 8 && blocks * kp < 512 && (H / 128) >= 2 * kp * 4) kp *= 2;
+  while (kp < kMaxParts && blocks * kp < 512 && (H / 128) >= 2 * kp * 4) kp *= 2;
   return kp;
 }
 
