@@ -235,17 +235,17 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
       // 2 * max(F, Fs)) or the output row (down, width H), fp32 ----
       const int64_t R = TK + a.T;
       const int width = MODE == 0 ? 2 * max(a.F, a.Fs) : a.H;
-  #pragma unroll
+#pragma unroll
       for (int n = 0; n < NN; ++n) {
         const int tr = 32 * n + r32;
         if (tr >= tl.rows) continue;
         float* dst = a.part + (static_cast<int64_t>(kp) * R + tl.row0 + tr) * width;
-  #pragma unroll
+#pragma unroll
         for (int m = 0; m < 4; ++m) {
           // gate_up: m = 0, 1 gate features, 2, 3 the same features' up rows
           const int col = MODE == 0 ? (m >> 1) * (width / 2) + o0 + 64 * wave + 32 * (m & 1)
                                     : o0 + 128 * wave + 32 * m;
-  #pragma unroll
+#pragma unroll
           for (int g = 0; g < 4; ++g)
             *reinterpret_cast<float4*>(dst + col + 8 * g + 4 * kh) =
                 make_float4(acc[m][n][4 * g], acc[m][n][4 * g + 1], acc[m][n][4 * g + 2], acc[m][n][4 * g + 3]);
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
 
     // ---- epilogue: lane holds rows 8*(i/4) + 4*kh + (i%4) of each 32-row
     // weight sub-tile, for grouped row 32*n + r32 ----
-  #pragma unroll
+#pragma unroll
     for (int n = 0; n < NN; ++n) {
       const int tr = 32 * n + r32;
       if (tr >= tl.rows) continue;
@@ -265,12 +265,12 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
         uint16_t* dst = sh ? static_cast<uint16_t*>(a.h_sh) + (p - TK) * a.Fs
                            : static_cast<uint16_t*>(a.h) + p * a.F;
         dst += o0 + 64 * wave + 4 * kh;
-  #pragma unroll
+#pragma unroll
         for (int m = 0; m < 2; ++m)
-  #pragma unroll
+#pragma unroll
           for (int g = 0; g < 4; ++g) {
             float h[4];
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) h[e] = silu(acc[m][n][4 * g + e]) * acc[m + 2][n][4 * g + e];
             uint2 v2;
             v2.x = pack_bf16(h[0], h[1]);
@@ -281,9 +281,9 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
         uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (p - TK) * a.H
                            : static_cast<uint16_t*>(a.y) + p * a.H;
         dst += o0 + 128 * wave + 4 * kh;
-  #pragma unroll
+#pragma unroll
         for (int m = 0; m < 4; ++m)
-  #pragma unroll
+#pragma unroll
           for (int g = 0; g < 4; ++g) {
             uint2 v2;
             v2.x = pack_bf16(acc[m][n][4 * g + 0], acc[m][n][4 * g + 1]);

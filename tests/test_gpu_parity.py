@@ -31,12 +31,15 @@ SMALL = [
     # 1, 7, 28 tokens: streamed work items of 16, 16, 32 rows; 40 .. 1100
     # tokens: the LDS-tiled kernels with the K loop split over 2-4 blocks (few
     # work items, ragged last tiles); 4096: tiled, no split; intermediate
-    # size 384 (not a multiple of the 256-row slab) at 100 tokens: streamed
-    # items of 64 rows
+    # size 384 (not a multiple of the 256-feature gate_up slab) at 100 and 40
+    # tokens and hidden size 640 (not a multiple of the 512-row down slab) at
+    # 100 tokens: streamed items of 64 and 32 rows
     (W["small_bf16"], 1), (W["small_bf16"], 7), (W["small_bf16"], 28), (W["small_bf16"], 40),
     (W["small_bf16"], 100), (W["small_bf16"], 256), (W["small_bf16"], 257), (W["small_bf16"], 300),
     (W["small_bf16"], 1024), (W["small_bf16"], 4096),
     (W["small_bf16"].replace(name="small_bf16_f384", moe_intermediate_size=384), 100),
+    (W["small_bf16"].replace(name="small_bf16_f384", moe_intermediate_size=384), 40),
+    (W["small_bf16"].replace(name="small_bf16_h640", hidden_size=640), 100),
     (W["small_bf16"].replace(name="small_bf16_e64", n_routed_experts=64), 1100),
     (W["small_grouped_bf16"], 100),
     (W["small_bf16"].replace(name="small_bf16_hot", bias="hot"), 300),
