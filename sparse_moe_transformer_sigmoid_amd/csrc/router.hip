@@ -78,7 +78,9 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const uint16_t* __rest
 // through LDS (144-byte padded rows, conflict-free 128-bit reads) one K step
 // of 64 ahead in registers; wave w owns tokens 32w..32w+31 x all 64 experts
 // (two 32x32x16 MFMA tiles, C[expert][token]).  Every router row is read
-// once per 128 tokens instead of once per 16.
+// once per 128 tokens instead of once per 16.  K part blockIdx.z of gridDim.z
+// covers steps [s0, s1) and writes its partial sums to logits + part * T * E
+// (added in part order by the top-k kernel).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void router_logits_bf16_tile(const uint16_t* __restrict__ x,
                                                                const uint16_t* __restrict__ wr,
@@ -104,16 +106,20 @@ __global__ __launch_bounds__(256) void router_logits_bf16_tile(const uint16_t* _
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
-  const int steps = H / 64;
+  const int steps = H / 64, per = (steps + gridDim.z - 1) / gridDim.z;
+  const int s0 = blockIdx.z * per, s1 = min(s0 + per, steps);
+  logits += static_cast<int64_t>(blockIdx.z) * T * E;
   uint4 st[6];
+  if (s0 < s1) {
 #pragma unroll
-  for (int c = 0; c < 6; ++c) st[c] = *reinterpret_cast<const uint4*>(src[c]);
+    for (int c = 0; c < 6; ++c) st[c] = *reinterpret_cast<const uint4*>(src[c] + s0 * 64);
 #pragma unroll
-  for (int c = 0; c < 6; ++c) *reinterpret_cast<uint4*>(&lds[0][ldo[c]]) = st[c];
+    for (int c = 0; c < 6; ++c) *reinterpret_cast<uint4*>(&lds[0][ldo[c]]) = st[c];
+  }
   __syncthreads();
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    const int ko = min(s + 1, steps - 1) * 64;
+  for (int s = s0; s < s1; ++s) {
+    const int buf = (s - s0) & 1;
+    const int ko = min(s + 1, s1 - 1) * 64;
 #pragma unroll
     for (int c = 0; c < 6; ++c) st[c] = *reinterpret_cast<const uint4*>(src[c] + ko);
     const uint16_t* bt = &lds[buf][(32 * wave + r32) * kLd + kh * 32];
@@ -279,17 +285,26 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
 // K parts of the 16x16 logits kernel: few tokens give few blocks (24 for one
 // token and 384 experts), so the K loop is split over up to 8 blocks per tile
 // until the grid has ~512 blocks; the top-k kernel adds the parts in order
+// K parts of the logits kernels: doubled while the grid has fewer than 512
+// blocks and every part keeps at least 4 K steps of 128 (16 x 16 kernel: one
+// per wave) or 8 of 64 (the 128 x 64 LDS-tiled kernel, whose blocks
+// otherwise walk all of H one latency-bound step at a time: at 512 tokens
+// and 384 experts its 24 blocks took 0.11 ms).
+bool router_tiled(int64_t T, int E, bool bf16) { return bf16 && T >= 512 && E % 64 == 0; }
+
 int router_kparts(int64_t T, int E, int H, bool bf16) {
-  if (!bf16 || (T >= 512 && E % 64 == 0)) return 1;
-  const int64_t blocks = static_cast<int64_t>((E + 15) / 16) * ((T + 15) / 16);
+  if (!bf16) return 1;
+  const bool tiled = router_tiled(T, E, bf16);
+  const int64_t blocks = tiled ? ((T + 127) / 128) * (E / 64) : static_cast<int64_t>((E + 15) / 16) * ((T + 15) / 16);
+  const int ksteps = tiled ? H / 64 : H / 128, min_steps = tiled ? 8 : 4;
   int kp = 1;
-  while (kp < kMaxParts && blocks * kp < 512 && (H / 128) >= 2 * kp * 4) kp *= 2;
+  while (kp < kMaxParts && blocks * kp < 512 && ksteps >= 2 * kp * min_steps) kp *= 2;
   return kp;
 }
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
-  if (a.bf16 && a.T >= 512 && a.E % 64 == 0) {
-    dim3 grid((a.T + 127) / 128, a.E / 64);
+  if (router_tiled(a.T, a.E, a.bf16)) {
+    dim3 grid((a.T + 127) / 128, a.E / 64, router_kparts(a.T, a.E, a.H, a.bf16));
     hipLaunchKernelGGL(router_logits_bf16_tile, grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.wr), a.T,
                        a.E, a.H, a.logits);

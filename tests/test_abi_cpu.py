@@ -67,10 +67,11 @@ def test_workspace_size_grows_with_tokens_and_matches_layout():
     c = k2cfg()
     s1, s128, s8192 = (B.moe_workspace_size(c, t) for t in (1, 128, 8192))
     assert 0 < s1 < s128 < s8192
-    # dominated by the per-row SwiGLU output and down output (bf16)
+    # dominated by the per-row SwiGLU output and down output (bf16); the rest
+    # (router partial logits of up to 8 K parts, grouping, work list) is small
     per_row = 8 * (2048 + 7168) * 2 + (2048 + 7168) * 2
     assert s8192 >= 8192 * per_row
-    assert s8192 < 8192 * per_row * 1.1
+    assert s8192 < 8192 * per_row * 1.15
     assert B.moe_workspace_size(k2cfg(hidden_size=100), 4) == 0
 
 
