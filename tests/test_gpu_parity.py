@@ -55,6 +55,15 @@ SMALL = [
     (W["small_fp8"].replace(name="small_fp8_h640", hidden_size=640), 100),
     (W["small_fp8"].replace(name="small_fp8_h640", hidden_size=640), 40),
     (W["small_fp8"].replace(name="small_fp8_hot", bias="hot"), 200),
+    # routing extremes: k = 32 (the largest supported), E = 1023 (the largest:
+    # 16 experts per lane in top-k, 1024 groups in the single-block
+    # grouping), 64 groups of 2 experts keeping 3, weights not renormalised
+    (W["small_bf16"].replace(name="small_bf16_k32", n_routed_experts=64, num_experts_per_tok=32), 50),
+    (W["small_bf16"].replace(name="small_bf16_e1023", n_routed_experts=1023, hidden_size=256,
+                             moe_intermediate_size=128), 64),
+    (W["small_bf16"].replace(name="small_bf16_g64", n_routed_experts=128, n_group=64, topk_group=3,
+                             num_experts_per_tok=6), 100),
+    (W["small_bf16"].replace(name="small_bf16_nonorm", norm_topk_prob=False, routed_scaling_factor=1.0), 100),
     (W["small_fp8"].replace(name="small_fp8_noshared", n_shared_experts=0), 50),
 ]
 
