@@ -3,19 +3,20 @@
 // ("Kimi K2 . Down projection", config.json quantization_config: fmt e4m3,
 // weight_block_size [128, 128], activation_scheme dynamic.)
 //
-// Same data movement as the bf16 tile kernel: both operands go global -> LDS
+// Data movement as in the bf16 tile kernel -- both operands go global -> LDS
 // by DMA (global_load_lds_dwordx4), 128-byte unpadded LDS rows with the slot
-// swizzle chunk ^ ((row >> 1) & 7), two stages held in separate __shared__
-// objects, the next step's DMA issues and the next row-tile's LDS reads
-// interleaved with the MFMAs, XCD-chunked order of (slab, tile) items.  A 128-byte
-// row is 128 fp8 K-elements: exactly one quantisation block per K step, so
-// each step is two v_mfma_scale_f32_32x32x64_f8f6f4 (unit e8m0 scales) per
-// 32x32 output tile into a fresh partial, added to the fp32 accumulator
-// scaled by weight-block scale x row scale:
+// swizzle chunk ^ ((row >> 1) & 7), XCD-chunked order of the work items --
+// but with three LDS stages, the DMA issued from inline asm and waited for
+// with counted s_waitcnt (the next step's DMA issues and the next row-tile's
+// LDS reads interleaved with the MFMAs).  A 128-byte row is 128 fp8
+// K-elements: exactly one quantisation block per K step, so each step is two
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit e8m0 scales) per 32x32 output tile
+// into a fresh partial, added to the fp32 accumulator scaled by weight-block
+// scale x row scale:
 //   acc += (sum_k q_w q_a) * s_w[block][kb] * s_a[row][kb].
 // The block is 256 weight rows x 128 grouped rows in 8 waves of 64 x 64.
-// gate_up writes the SwiGLU output in fp32 (re-quantised per row and 128
-// channels before the down projection); down writes bf16.
+// gate_up writes the SwiGLU output already quantised for the down projection
+// (e4m3 codes + one scale per row and 128 channels); down writes bf16.
 #include "kernels.h"
 
 namespace moe {
@@ -69,8 +70,7 @@ __device__ __forceinline__ f32x16 mma_fp8_32(const uint4& a0, const uint4& a1, c
 // of its partial products (VALU), the other's MFMAs run.
 template <int MODE>
 __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
-  // two stages as separate objects (no alias between a DMA into one and the
-  // LDS reads of the other, as in the bf16 tile kernel)
+  // three stages as separate objects
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t st2[kStage];
@@ -268,39 +268,75 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
 
   // ---- epilogue: lane holds weight rows 8*(i/4) + 4*kh + (i%4) of each
   // 32-row tile, for grouped row 64*wn + 32*n + r32 ----
+  if (MODE == 0) {
+    // h = SiLU(gate) * up, quantised here for the down projection: the slab's
+    // 128 features are one 128-channel group ("Kimi K2 . Down projection",
+    // activation_scheme dynamic), held by the four waves wm of a row half
+    // wn, 16 values per lane.  s = amax / 448 (1 for an all-zero group),
+    // codes e4m3(h / s) with the division in fp32 -- the same arithmetic as
+    // the activation-quant kernel.  The row maxima meet in LDS (stage 0 is
+    // free once the K loop has drained).
+    float hv[2][16], rmax[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        hv[n][i] = silu(acc[0][n][i]) * acc[1][n][i];
+        m = fmaxf(m, fabsf(hv[n][i]));
+      }
+      rmax[n] = fmaxf(m, __shfl_xor(m, 32, 64));
+    }
+    float* gmax = reinterpret_cast<float*>(st0);   // [4 wm][128 rows]
+    if (kh == 0) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n) gmax[128 * wm + 64 * wn + 32 * n + r32] = rmax[n];
+    }
+    __syncthreads();
+    const int64_t gidx = o0 / 128;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int tr = 64 * wn + 32 * n + r32;
+      if (tr >= tl.rows) continue;
+      const float amax = fmaxf(fmaxf(gmax[tr], gmax[128 + tr]), fmaxf(gmax[256 + tr], gmax[384 + tr]));
+      const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+      const int64_t p = tl.row0 + tr;
+      uint8_t* dst = sh ? static_cast<uint8_t*>(a.hq_sh) + (p - TK) * a.Fs : static_cast<uint8_t*>(a.hq) + p * a.F;
+      dst += o0 + 32 * wm + 4 * kh;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c |= static_cast<uint32_t>(f32_to_e4m3(hv[n][4 * g + e] / sc)) << (8 * e);
+        *reinterpret_cast<uint32_t*>(dst + 8 * g) = c;
+      }
+      if (wm == 0 && kh == 0) {
+        float* sdst = sh ? a.h_sh_scales + (p - TK) * (a.Fs / 128) : a.h_scales + p * (a.F / 128);
+        sdst[gidx] = sc;
+      }
+    }
+    return;
+  }
+  // down: y in bf16
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int tr = 64 * wn + 32 * n + r32;
     if (tr >= tl.rows) continue;
     const int64_t p = tl.row0 + tr;
-    if (MODE == 0) {
-      float* dst = sh ? static_cast<float*>(a.h_sh) + (p - TK) * a.Fs : static_cast<float*>(a.h) + p * a.F;
-      dst += o0 + 32 * wm + 4 * kh;
+    uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (p - TK) * a.H
+                       : static_cast<uint16_t*>(a.y) + p * a.H;
+    dst += o0 + 64 * wm + 4 * kh;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float4 h;
-        h.x = silu(acc[0][n][4 * g + 0]) * acc[1][n][4 * g + 0];
-        h.y = silu(acc[0][n][4 * g + 1]) * acc[1][n][4 * g + 1];
-        h.z = silu(acc[0][n][4 * g + 2]) * acc[1][n][4 * g + 2];
-        h.w = silu(acc[0][n][4 * g + 3]) * acc[1][n][4 * g + 3];
-        *reinterpret_cast<float4*>(dst + 8 * g) = h;
+        uint2 v2;
+        v2.x = static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 0])) |
+               (static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 1])) << 16);
+        v2.y = static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 2])) |
+               (static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 3])) << 16);
+        *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g) = v2;
       }
-    } else {
-      uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (p - TK) * a.H
-                         : static_cast<uint16_t*>(a.y) + p * a.H;
-      dst += o0 + 64 * wm + 4 * kh;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 v2;
-          v2.x = static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 0])) |
-                 (static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 1])) << 16);
-          v2.y = static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 2])) |
-                 (static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 3])) << 16);
-          *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g) = v2;
-        }
-    }
   }
 }
 
@@ -323,14 +359,9 @@ static hipError_t launch_tile_fp8(const FfnArgs& a, int slabs, hipStream_t st) {
   return hipGetLastError();
 }
 
+// gate_up writes h already quantised (e4m3 codes + per-128 scales)
 hipError_t launch_gate_up_tile_fp8(const FfnArgs& a, hipStream_t st) {
-  hipError_t e = launch_tile_fp8<0>(a, std::max(a.F, a.Fs) / (kBW / 2), st);
-  if (e != hipSuccess) return e;
-  e = launch_act_quant_f32(static_cast<const float*>(a.h), static_cast<int64_t>(a.T) * a.k, a.F,
-                           static_cast<uint8_t*>(a.hq), a.h_scales, st);
-  if (e != hipSuccess || a.Fs == 0) return e;
-  return launch_act_quant_f32(static_cast<const float*>(a.h_sh), a.T, a.Fs, static_cast<uint8_t*>(a.hq_sh),
-                              a.h_sh_scales, st);
+  return launch_tile_fp8<0>(a, std::max(a.F, a.Fs) / (kBW / 2), st);
 }
 
 hipError_t launch_down_tile_fp8(const FfnArgs& a, hipStream_t st) {
