@@ -158,8 +158,11 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
     }
   };
 
-  // this block's K steps [s0, s0 + steps); steps is even
-  const int steps = K / kBK / ks, s0 = kp * steps;
+  // this block's K steps [s0, s0 + steps): part kp of ks parts of `kper`
+  // steps (even), the last part shorter; every part is non-empty
+  // (tile_ksplit) and even, since K / 64 is even
+  const int ksteps = K / kBK, kper = ((ksteps + ks - 1) / ks + 1) & ~1;
+  const int s0 = kp * kper, steps = min(kper, ksteps - s0);
   const int sw = (r32 >> 1) & 7;                       // row swizzle of this lane's rows
   const int arow = (128 * wave + r32) * kRowB;
   const int brow = (kBW + r32) * kRowB;
@@ -342,23 +345,33 @@ __global__ __launch_bounds__(256) void ffn_split_finish(FfnArgs a, int ks) {
 
 int tile_rows() { return kBM; }
 
-// K parts of the tiled kernels for a grid of `blocks` (slabs x work items):
-// doubled (up to max_ks) while the grid has fewer than `target` blocks (the
-// kernel holds a whole CU's LDS, so 256 blocks fill the chip), keeping every
-// part an even number of 64-wide steps of both K1 and K2.  With `one_round`
-// the doubled grid must still fit in `target` blocks: a grid just past one
-// round of the chip runs two rounds of half-length blocks plus twice the
-// partial sums.  Measured on MI355X: gate_up (one_round, 256): 72 blocks
-// (one expert-parallel rank's 3 experts, the dense layer's one) take 0.142 /
-// 0.166 ms with 2 parts against 0.158 / 0.195 ms with 4; down (128, fp32
-// partial sums 7168 wide): the dense layer's 14 blocks gain up to 16 parts
-// (0.10 ms against 0.154 with 4), while at 140 blocks the extra pass cost
-// more than the split gained.
+// K parts of the tiled kernels for a grid of `blocks` (slabs x work items).
+// The kernel holds a whole CU's LDS, so 256 blocks fill the chip.
+//  * one_round (gate_up): as many parts as keep the grid within one round
+//    of `target` blocks, of any count (parts of an even number of 64-wide
+//    steps, the last one shorter).  A grid just past one round runs two
+//    rounds of shorter blocks plus more partial sums: one expert-parallel
+//    rank's 3 experts (72 blocks) took 0.142 ms with 2 parts against 0.158
+//    with 4.
+//  * otherwise (down, fp32 partial sums 7168 wide): doubled while the grid
+//    has fewer than `target` blocks and every part keeps a multiple of 4
+//    steps of both K1 and K2: the dense layer's 14 blocks gain up to 16 parts
+//    (0.10 ms against 0.154 with 4), while at 140 blocks the extra pass cost
+//    more than the split gained.
 int tile_ksplit(int64_t blocks, int K1, int K2, int max_ks, int target, bool one_round) {
+  if (one_round) {
+    // every part non-empty: (ks - 1) parts of per = ceil_even(steps / ks)
+    // steps leave at least one step for the last
+    auto valid = [](int K, int ks) {
+      const int n = K / kBK, per = ((n + ks - 1) / ks + 1) & ~1;
+      return (ks - 1) * per < n;
+    };
+    int ks = static_cast<int>(std::min<int64_t>(max_ks, std::max<int64_t>(1, target / blocks)));
+    while (ks > 1 && !(valid(K1, ks) && valid(K2, ks))) --ks;
+    return ks;
+  }
   int ks = 1;
-  while (ks < max_ks && blocks * (one_round ? 2 * ks : ks) <= (one_round ? target : target - 1) &&
-         (K1 / kBK) % (4 * ks) == 0 && (K2 / kBK) % (4 * ks) == 0)
-    ks *= 2;
+  while (ks < max_ks && blocks * ks < target && (K1 / kBK) % (4 * ks) == 0 && (K2 / kBK) % (4 * ks) == 0) ks *= 2;
   return ks;
 }
 

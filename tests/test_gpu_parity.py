@@ -40,6 +40,9 @@ SMALL = [
     (W["small_bf16"].replace(name="small_bf16_f384", moe_intermediate_size=384), 100),
     (W["small_bf16"].replace(name="small_bf16_f384", moe_intermediate_size=384), 40),
     (W["small_bf16"].replace(name="small_bf16_h640", hidden_size=640), 100),
+    # hidden size 2560 (40 K steps of 64) at 40 tokens: gate_up split over 7
+    # K parts of 6, 6, 6, 6, 6, 6 and 4 steps
+    (W["small_bf16"].replace(name="small_bf16_h2560", hidden_size=2560), 40),
     (W["small_bf16"].replace(name="small_bf16_e64", n_routed_experts=64), 1100),
     (W["small_grouped_bf16"], 100),
     (W["small_bf16"].replace(name="small_bf16_hot", bias="hot"), 300),
