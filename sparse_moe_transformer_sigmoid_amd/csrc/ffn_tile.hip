@@ -346,13 +346,16 @@ __global__ __launch_bounds__(256) void ffn_split_finish(FfnArgs a, int ks) {
 int tile_rows() { return kBM; }
 
 // K parts of the tiled kernels for a grid of `blocks` (slabs x work items).
-// The kernel holds a whole CU's LDS, so 256 blocks fill the chip.
-//  * one_round (gate_up): as many parts as keep the grid within one round
-//    of `target` blocks, of any count (parts of an even number of 64-wide
-//    steps, the last one shorter).  A grid just past one round runs two
-//    rounds of shorter blocks plus more partial sums: one expert-parallel
-//    rank's 3 experts (72 blocks) took 0.142 ms with 2 parts against 0.158
-//    with 4.
+// The kernel holds a whole CU's LDS, so 256 blocks make one round of the
+// chip.
+//  * one_round (gate_up), for a grid under one round of `target` blocks:
+//    the fewest parts (any count: parts of an even number of 64-wide steps,
+//    the last one shorter) for which the grid's last round is at least 80 %
+//    full.  A half-empty last round costs a whole round; more parts cost
+//    partial sums and shorter blocks.  Measured: one expert-parallel rank's
+//    3 experts (80 blocks): 0.158 ms with 4 parts, 0.142 with 2, 0.120 with
+//    3.  Grids past one round are not split: for 48 experts (392 blocks,
+//    1.5 rounds) 3 parts gained nothing (0.578 ms against 0.581).
 //  * otherwise (down, fp32 partial sums 7168 wide): doubled while the grid
 //    has fewer than `target` blocks and every part keeps a multiple of 4
 //    steps of both K1 and K2: the dense layer's 14 blocks gain up to 16 parts
@@ -360,15 +363,26 @@ int tile_rows() { return kBM; }
 //    more than the split gained.
 int tile_ksplit(int64_t blocks, int K1, int K2, int max_ks, int target, bool one_round) {
   if (one_round) {
+    if (blocks >= target) return 1;
     // every part non-empty: (ks - 1) parts of per = ceil_even(steps / ks)
     // steps leave at least one step for the last
     auto valid = [](int K, int ks) {
       const int n = K / kBK, per = ((n + ks - 1) / ks + 1) & ~1;
       return (ks - 1) * per < n;
     };
-    int ks = static_cast<int>(std::min<int64_t>(max_ks, std::max<int64_t>(1, target / blocks)));
-    while (ks > 1 && !(valid(K1, ks) && valid(K2, ks))) --ks;
-    return ks;
+    int best = 1;
+    double best_fill = 0.0;
+    for (int ks = 1; ks <= max_ks; ++ks) {
+      if (!(valid(K1, ks) && valid(K2, ks))) break;
+      const int64_t n = blocks * ks, rounds = (n + target - 1) / target;
+      const double fill = static_cast<double>(n) / static_cast<double>(rounds * target);
+      if (fill >= 0.8) return ks;
+      if (fill > best_fill) {
+        best_fill = fill;
+        best = ks;
+      }
+    }
+    return best;
   }
   int ks = 1;
   while (ks < max_ks && blocks * ks < target && (K1 / kBK) % (4 * ks) == 0 && (K2 / kBK) % (4 * ks) == 0) ks *= 2;
