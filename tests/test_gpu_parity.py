@@ -437,6 +437,38 @@ def test_layer_replays_from_a_graph(name, block):
         assert torch.equal(out, ref_out) and torch.equal(ids, ref_ids) and torch.equal(wts, ref_w)
 
 
+@pytest.mark.parametrize("name,T", [("small_bf16", 300), ("small_bf16", 7), ("small_fp8", 100)])
+def test_concurrent_calls_on_two_streams(name, T):
+    """The library keeps no state between calls beyond the caller's buffers:
+    two layer calls in flight at once on two streams, each with its own
+    workspace and a different input, give the same bits as each call alone."""
+    wl = W[name]
+    case = small_case(wl, T)
+    cfg = B.MoeConfig.from_fields(wl.fields())
+    weights = B.MoeWeights.from_tensors(case)
+    xs = [case["x"], case["x"].flip(0).contiguous()]
+    refs = []
+    for xin in xs:
+        c = dict(case)
+        c["x"] = xin
+        refs.append(run_layer(wl, c))
+    k = wl.num_experts_per_tok
+    outs = [(torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda"),
+             torch.empty((T, k), dtype=torch.int32, device="cuda"),
+             torch.empty((T, k), dtype=torch.float32, device="cuda")) for _ in xs]
+    wss = [B.alloc_workspace(cfg, T) for _ in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                o, ids, w = outs[i]
+                B.moe_layer_forward(cfg, weights, xs[i], case["router_w"], case["router_bias"], o, wss[i], ids, w)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert all(torch.equal(a, b) for a, b in zip(outs[i], refs[i])), f"stream {i}, pass {rep}"
+
+
 def test_k2_max_tokens_full_size(k2_weights):
     """The largest batch the ABI takes (65536 tokens, 524288 grouped rows:
     row offsets past 2^31 elements): routing of every token and the
