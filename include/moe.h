@@ -188,8 +188,11 @@ int moe_abi_version(void);
 enum {
   MOE_KID_ROUTER_LOGITS = 0, /* x W_r^T                                        */
   MOE_KID_ROUTER_TOPK = 1,   /* sigmoid, bias, groups, top-k, weights          */
-  MOE_KID_PERMUTE = 2,       /* histogram + scan + stable scatter (3 kernels)  */
-  MOE_KID_TILES = 3,         /* work list of the grouped GEMMs                 */
+  MOE_KID_PERMUTE = 2,       /* histogram + scan + stable scatter: 3 kernels,
+                                one up to 256 tokens (in the layer it also
+                                writes the work list)                          */
+  MOE_KID_TILES = 3,         /* work list of the grouped GEMMs (when not
+                                written by the grouping kernel)               */
   MOE_KID_GATHER = 4,        /* x_perm rows (moe_permute only)                 */
   MOE_KID_ACT_QUANT = 5,     /* fp8 activation quantisation of x               */
   MOE_KID_GATE_UP = 6,       /* grouped gate/up GEMM + SiLU * up               */
