@@ -283,17 +283,42 @@ def measure(cfg, weights, wl, case, T, steps, warmup, hip, factory=make_step):
             eager()
         torch.cuda.synchronize()
     gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))  # every eager step launches it
-    return eager, wall, gate_up_ms, n_active
+    return eager, step, wall, gate_up_ms, n_active
 
 
-def layer_bytes(wl, T, n_active):
+def layer_bytes(wl, T, n_active, router=True):
     """Algorithmic HBM bytes of one layer step: every active expert's and the
-    shared expert's weights once, the router, x in and out."""
+    shared expert's weights once, the router (unless `router` is false), x in
+    and out."""
     F, Fs, H, E = wl.moe_intermediate_size, wl.shared_intermediate_size, wl.hidden_size, wl.n_routed_experts
     per = weight_bytes_per_expert_gate_up(wl, F) * 3 // 2
     sh = weight_bytes_per_expert_gate_up(wl, Fs) * 3 // 2 if Fs else 0
     act = 2 if wl.act_dtype == gen.BF16 else 4
-    return n_active * per + sh + E * H * act + 4 * E + 2 * T * H * act
+    return n_active * per + sh + (E * H * act + 4 * E if router else 0) + 2 * T * H * act
+
+
+def layer_flops(wl, T, routed_rows=None):
+    """Algorithmic flops of one layer step: 2 * 3 * H * F per routed row and
+    2 * 3 * H * Fs per token for the shared expert, plus the router's 2*T*H*E
+    (padded tile rows and skipped experts not counted)."""
+    F, Fs, H, E, k = (wl.moe_intermediate_size, wl.shared_intermediate_size, wl.hidden_size,
+                      wl.n_routed_experts, wl.num_experts_per_tok)
+    rows = T * k if routed_rows is None else routed_rows
+    router = 0 if routed_rows is not None else 2.0 * T * H * E
+    return 6.0 * H * (rows * F + T * Fs) + router
+
+
+def layer_roofline(wl, T, n_active, ms, routed_rows=None):
+    """Whole-layer fractions of the HBM and MFMA peaks, and which one binds:
+    max(t_bytes, t_flops) / t."""
+    by = layer_bytes(wl, T, n_active, router=routed_rows is None)   # a rank's FFN share has no router
+    if routed_rows is not None:   # ... but reads and writes its dispatched rows as well
+        by += 2 * routed_rows * wl.hidden_size * (2 if wl.act_dtype == gen.BF16 else 4)
+    fl = layer_flops(wl, T, routed_rows)
+    sec = ms * 1e-3
+    t_b, t_f = by / (PEAK_HBM_GBS * 1e9), fl / (PEAK_TFLOPS[wl.weight_dtype] * 1e12)
+    return {"bytes": by, "flops": fl, "hbm_frac": round(t_b / sec, 4), "mfma_frac": round(t_f / sec, 4),
+            "binding": "hbm" if t_b >= t_f else "mfma", "binding_frac": round(max(t_b, t_f) / sec, 4)}
 
 
 def sweep(args, wl, case, cfg, weights, hip):
@@ -304,7 +329,7 @@ def sweep(args, wl, case, cfg, weights, hip):
     for T in [int(t) for t in args.sweep_tokens.split(",")]:
         c = dict(case)
         c["x"] = gen.gen_x(wl, T).cuda()
-        _, wall, gu_ms, n_act = measure(cfg, weights, wl, c, T, args.steps, args.warmup, hip)
+        _, _, wall, gu_ms, n_act = measure(cfg, weights, wl, c, T, args.steps, args.warmup, hip)
         ms = wall * 1e3 / args.steps
         by = layer_bytes(wl, T, n_act)
         rec = {"workload": wl.name, "num_tokens": T, "ms_per_step": round(ms, 4),
@@ -362,7 +387,7 @@ def main():
         case = setup(wl, T)
         cfg = B.MoeConfig.from_fields(wl.fields())
     weights = B.MoeWeights.from_tensors(case)
-    step, wall, gate_up_ms, n_active = measure(cfg, weights, wl, case, T, args.steps, args.warmup, hip,
+    step, timed_step, wall, gate_up_ms, n_active = measure(cfg, weights, wl, case, T, args.steps, args.warmup, hip,
                                                make_rank_step if rank else make_step)
     if rank:
         n_active = n_local
@@ -395,6 +420,16 @@ def main():
         torch.cuda.synchronize()
 
     rl = roofline(wl, T, n_active, gate_up_ms, stored_traffic(args.workload, T), routed_rows)
+    # spread of 20 single steps after the timed region, launched as the timed
+    # ones were (the timed figure is the mean over exactly `steps` back-to-back steps)
+    singles = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        timed_step()
+        e1.record()
+        e1.synchronize()
+        singles.append(e0.elapsed_time(e1))
     res = {
         "metric": METRIC, "value": round(T * args.steps / wall, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -407,6 +442,8 @@ def main():
                    "parallelism": "none (one GPU, all experts resident)",
                    "launch": "eager" if args.eager else "hip graph replay (one captured layer step)"},
         "roofline": rl,
+        "layer_roofline": layer_roofline(wl, T, n_active, ms_per_step, routed_rows),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(singles, q)), 4) for q in (10, 50, 90)],
     }
     if rank:
         res["config"].update(parallelism=f"one rank of ep{wl.ep_size} (its expert FFN share only)",
