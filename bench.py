@@ -2,7 +2,8 @@
 """Benchmark of the Kimi-K2 routed MoE FFN layer on one MI355X.
 
 One step = one moe_layer_forward (router, grouping, expert FFNs, combine) over
-one batch of synthetic tokens whose inputs are already resident in HBM.
+one batch of synthetic tokens whose inputs are already resident in HBM; steps
+rotate among 4 such batches.
 Default workload: Kimi-K2 decode, T = 128 tokens, bf16, all 384 experts + 1
 shared resident.  A step is captured once in a HIP graph and replayed (the
 library only launches kernels: no memset, no host synchronisation); --eager
@@ -77,9 +78,15 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+X_BATCHES = 4
+
+
 def setup(wl: gen.Workload, T: int):
-    x = gen.gen_x(wl, T).cuda()
-    d = {"x": x, "router_w": gen.gen_router(wl).cuda(), "router_bias": gen.gen_bias(wl).cuda(),
+    """Resident inputs: X_BATCHES independent token batches (steps rotate
+    among them, so no step finds its x, and the routing it causes, cached
+    from the step before), the router and the expert weights."""
+    xs = [gen.gen_x(wl, T, b).cuda() for b in range(X_BATCHES)]
+    d = {"x": xs[0], "xs": xs, "router_w": gen.gen_router(wl).cuda(), "router_bias": gen.gen_bias(wl).cuda(),
          "norm_weight": gen.gen_norm_weight(wl).cuda()}
     d.update(gen.gen_expert_weights(wl, device="cuda"))
     torch.cuda.synchronize()
@@ -99,7 +106,7 @@ def roofline(wl: gen.Workload, T: int, n_active: int, gate_up_ms: float, traffic
     2 * 2 * rows * H * F for the gate and up products (flops)."""
     F, Fs, H, k = wl.moe_intermediate_size, wl.shared_intermediate_size, wl.hidden_size, wl.num_experts_per_tok
     rows = T * k if routed_rows is None else routed_rows
-    bytes_ = n_active * weight_bytes_per_expert_gate_up(wl, F)
+    bytes_ = round(n_active * weight_bytes_per_expert_gate_up(wl, F))
     if Fs:
         bytes_ += weight_bytes_per_expert_gate_up(wl, Fs)
     flops = 4.0 * (rows * F + T * Fs) * H
@@ -214,25 +221,39 @@ def make_rank_step(cfg, weights, wl, case, T):
 
     def step():
         B.moe_expert_ffn(cfg, weights, case["x"], case["x_rows"], None, case["offsets"], y, y_sh, ws)
-    return step, None
+    return [step], None
 
 
 def make_step(cfg, weights, wl, case, T):
-    """One layer step on pre-allocated buffers (inputs resident in HBM)."""
-    out = torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda")
-    ids = torch.empty((T, wl.num_experts_per_tok), dtype=torch.int32, device="cuda")
-    wts = torch.empty((T, wl.num_experts_per_tok), dtype=torch.float32, device="cuda")
+    """One layer step per resident token batch, on pre-allocated buffers
+    (inputs resident in HBM); returns the steps and each batch's ids."""
     ws = B.alloc_workspace(cfg, T)
-
     eps = float(np.float32(wl.rms_norm_eps))
+    steps, ids_all = [], []
+    for x in case["xs"]:
+        out = torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda")
+        ids = torch.zeros((T, wl.num_experts_per_tok), dtype=torch.int32, device="cuda")
+        wts = torch.empty((T, wl.num_experts_per_tok), dtype=torch.float32, device="cuda")
 
-    def step():
-        if wl.block:
-            B.moe_block_forward(cfg, weights, case["x"], case["norm_weight"], eps, case["router_w"],
-                                case["router_bias"], out, ws, ids, wts)
-        else:
-            B.moe_layer_forward(cfg, weights, case["x"], case["router_w"], case["router_bias"], out, ws, ids, wts)
-    return step, ids
+        def step(x=x, out=out, ids=ids, wts=wts):
+            if wl.block:
+                B.moe_block_forward(cfg, weights, x, case["norm_weight"], eps, case["router_w"],
+                                    case["router_bias"], out, ws, ids, wts)
+            else:
+                B.moe_layer_forward(cfg, weights, x, case["router_w"], case["router_bias"], out, ws, ids, wts)
+        steps.append(step)
+        ids_all.append(ids)
+    return steps, ids_all
+
+
+def rotate(fns):
+    """A callable that runs fns[0], fns[1], ... in turn, one per call."""
+    state = {"i": 0}
+
+    def run():
+        fns[state["i"] % len(fns)]()
+        state["i"] += 1
+    return run
 
 
 def graphed(step):
@@ -256,20 +277,23 @@ GRAPH = False
 
 def measure(cfg, weights, wl, case, T, steps, warmup, hip, factory=make_step):
     """Time `steps` layer steps after `warmup` untimed ones (synchronised on
-    both sides); the gate_up launch of every timed step is bracketed by HIP
-    events the library records on its own stream (not with --graph, whose
-    replays record no events: gate_up is then timed on as many eager steps
-    after the graph's timed region)."""
-    step, ids = factory(cfg, weights, wl, case, T)
-    eager = step
-    if GRAPH:
-        step = graphed(step)
+    both sides), the steps rotating among the resident token batches; the
+    gate_up launch of every timed step is bracketed by HIP events the library
+    records on its own stream (not with graph replay, which records no
+    events: gate_up is then timed on as many eager steps after the timed
+    region).  Before the timed region a 512 MB buffer is written, so the
+    256 MB MALL holds none of the inputs.  n_active is the mean over the
+    batches of the experts their tokens select."""
+    fns, ids = factory(cfg, weights, wl, case, T)
+    eager = rotate(fns)
+    step = rotate([graphed(f) for f in fns]) if GRAPH else eager
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    n_active = int(torch.unique(ids).numel()) if ids is not None else None
     evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush.fill_(1)
     torch.cuda.synchronize()
+    del flush
     t0 = time.perf_counter()
     for i in range(steps):
         if not GRAPH:
@@ -283,6 +307,12 @@ def measure(cfg, weights, wl, case, T, steps, warmup, hip, factory=make_step):
             eager()
         torch.cuda.synchronize()
     gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))  # every eager step launches it
+    n_active = None
+    if ids is not None:
+        for f in fns:   # every batch once more, so that each one's ids are there
+            f()
+        torch.cuda.synchronize()
+        n_active = float(np.mean([torch.unique(i).numel() for i in ids]))
     return eager, step, wall, gate_up_ms, n_active
 
 
@@ -294,7 +324,7 @@ def layer_bytes(wl, T, n_active, router=True):
     per = weight_bytes_per_expert_gate_up(wl, F) * 3 // 2
     sh = weight_bytes_per_expert_gate_up(wl, Fs) * 3 // 2 if Fs else 0
     act = 2 if wl.act_dtype == gen.BF16 else 4
-    return n_active * per + sh + (E * H * act + 4 * E if router else 0) + 2 * T * H * act
+    return round(n_active * per) + sh + (E * H * act + 4 * E if router else 0) + 2 * T * H * act
 
 
 def layer_flops(wl, T, routed_rows=None):
@@ -328,7 +358,7 @@ def sweep(args, wl, case, cfg, weights, hip):
     recs = []
     for T in [int(t) for t in args.sweep_tokens.split(",")]:
         c = dict(case)
-        c["x"] = gen.gen_x(wl, T).cuda()
+        c["xs"] = [gen.gen_x(wl, T, b).cuda() for b in range(X_BATCHES)]
         _, _, wall, gu_ms, n_act = measure(cfg, weights, wl, c, T, args.steps, args.warmup, hip)
         ms = wall * 1e3 / args.steps
         by = layer_bytes(wl, T, n_act)
@@ -440,7 +470,7 @@ def main():
                    "num_experts_per_tok": wl.num_experts_per_tok, "n_shared_experts": wl.n_shared_experts,
                    "n_group": wl.n_group, "topk_group": wl.topk_group, "active_experts": n_active,
                    "parallelism": "none (one GPU, all experts resident)",
-                   "launch": "eager" if args.eager else "hip graph replay (one captured layer step)"},
+                   "launch": "eager" if args.eager else "hip graph replay (one captured layer step per token batch)"},
         "roofline": rl,
         "layer_roofline": layer_roofline(wl, T, n_active, ms_per_step, routed_rows),
         "step_ms_p10_p50_p90": [round(float(np.percentile(singles, q)), 4) for q in (10, 50, 90)],

@@ -179,9 +179,12 @@ def gen_x_rows(wl: Workload, rows: np.ndarray, attempt: int) -> torch.Tensor:
     return round_to(out, wl.act_dtype)
 
 
-def gen_x(wl: Workload, num_tokens: Optional[int] = None) -> torch.Tensor:
+def gen_x(wl: Workload, num_tokens: Optional[int] = None, batch: int = 0) -> torch.Tensor:
+    """Token rows x ~ N(0, 1); batch b > 0 draws an independent batch of the
+    same shape (a benchmark rotates among several)."""
     T = wl.num_tokens if num_tokens is None else num_tokens
-    a = _rng(wl.seed, TID_X).standard_normal((T, wl.hidden_size), np.float32)
+    rng = _rng(wl.seed, TID_X) if batch == 0 else _rng(wl.seed, TID_X, batch)
+    a = rng.standard_normal((T, wl.hidden_size), np.float32)
     return round_to(a, wl.act_dtype)
 
 
