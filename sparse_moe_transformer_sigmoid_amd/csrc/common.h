@@ -12,6 +12,15 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+// 16-byte load with the nontemporal hint (global_load_dwordx4 ... nt), for
+// weight bytes read once, in instructions that each cover whole 128-byte
+// lines (with partly covered lines the hint costs re-fetches).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 constexpr int kWave = 64;
 

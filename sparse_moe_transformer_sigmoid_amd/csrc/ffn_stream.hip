@@ -9,10 +9,12 @@
 // long weight dimension is the MFMA M side and up to 16 grouped rows (tokens)
 // form N.  A block is 4 waves that split the K loop of one 16-row (gate_up:
 // 16 gate + 16 up rows) or 64-row (down; 32-row for 64-row work items)
-// weight slab; every lane streams 64
-// contiguous bytes of one weight row per K step of 128 (16x16x32 bf16 MFMA,
-// the K order inside a step permuted the same way for both operands), so each
-// weight byte is read exactly once per tile of 16 rows.  The four partial sums
+// weight slab, K steps of 128 (64 for 64-row items) dealt round-robin to
+// the waves.  The weights are loaded in whole 128-byte lines per instruction
+// with the nontemporal hint and pass through a per-wave LDS scratch into the
+// MFMA layout (16x16x32 bf16; the K order inside a step permuted the same way
+// for both operands); each weight byte is read exactly once per tile of 16
+// rows.  The four partial sums
 // meet in LDS in a fixed order (deterministic).  Grid: x = weight slab, y =
 // work-list tile; tiles past the device-side count exit at once.
 #include "kernels.h"
@@ -23,13 +25,21 @@ namespace {
 
 constexpr int kWK = 4;  // waves splitting K
 
-// K elements per wave step: 128 for up to 32 rows, then halved as the row
-// sub-tiles grow so that the double-buffered fragments stay in registers
+// K elements per wave step: 128 for up to 32 rows, 64 for 64-row items, so
+// that the double-buffered operands stay in registers
 template <int NT>
-constexpr int step_k() { return NT <= 2 ? 128 : (NT == 4 ? 64 : 32); }
+constexpr int step_k() { return NT <= 2 ? 128 : 64; }
 
-// One wave's operands for one K step: NA weight row-tiles and NT token
-// sub-tiles of 16 rows, KS / 32 uint4 (8 bf16) per lane and row.
+// One wave's operands for one K step.
+//  a: NA weight row-tiles of 16 rows as loaded -- each load instruction
+//     covers 8 rows x 128 contiguous bytes (lane L: row L / 8 (+ 8 for the
+//     second row group), 16-byte chunk L % 8 of a 128-byte line), the
+//     nontemporal form: full lines per instruction stream from HBM at
+//     ~7.1 TB/s against ~5.9 for 64 bytes of each of 16 rows per instruction
+//     (16 GB reads shaped like these slabs, on MI355X).  Load j of a tile is
+//     row group j % 2, line j / 2.
+//  b: NT token sub-tiles of 16 rows in the MFMA layout: lane (r = L % 16,
+//     q = L / 16) holds elements 32 i + 8 q + [0, 8) of row r for MFMA i.
 template <int NA, int NT, int KS>
 struct Frag {
   uint4 a[NA][KS / 32];
@@ -38,43 +48,76 @@ struct Frag {
 
 template <int NA, int NT, int KS>
 __device__ __forceinline__ void load_frag(Frag<NA, NT, KS>& f, const uint16_t* const (&pa)[NA],
-                                          const uint16_t* const (&pb)[NT], int koff) {
+                                          const uint16_t* const (&pb)[NT], int64_t ld8, int koff) {
 #pragma unroll
-  for (int m = 0; m < NA; ++m) {
-    const uint4* s = reinterpret_cast<const uint4*>(pa[m] + koff);
+  for (int m = 0; m < NA; ++m)
 #pragma unroll
-    for (int i = 0; i < KS / 32; ++i) f.a[m][i] = s[i];
-  }
+    for (int j = 0; j < KS / 32; ++j)
+      f.a[m][j] = load_nt(reinterpret_cast<const uint4*>(pa[m] + (j & 1) * ld8 + koff + (j >> 1) * 64));
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const uint4* s = reinterpret_cast<const uint4*>(pb[n] + koff);
 #pragma unroll
-    for (int i = 0; i < KS / 32; ++i) f.b[n][i] = s[i];
+    for (int i = 0; i < KS / 32; ++i) f.b[n][i] = s[4 * i];
   }
 }
 
+// Per-wave LDS scratch that turns the loaded weight layout into the MFMA
+// layout: row rho (0..15) of tile m holds KS / 8 16-byte chunks, chunk c at
+// slot c ^ swz(rho).  The swizzle keeps both the 8-row x 8-chunk writes and
+// the 16-row reads of one chunk free of bank conflicts (16 lanes of 16 bytes
+// per LDS cycle): rows 256 B apart (KS = 128) differ in their slot, rows
+// 128 B apart (KS = 64) pair up by parity.
+template <int KS>
+__device__ __forceinline__ int swz(int rho) {
+  return KS == 128 ? (rho ^ ((rho & 1) << 3)) : ((rho >> 1) & 7);
+}
+
 template <int NA, int NT, int KS>
-__device__ __forceinline__ void mma_frag(const Frag<NA, NT, KS>& f, f32x4 (&acc)[NA][NT]) {
+__device__ __forceinline__ void mma_frag(const Frag<NA, NT, KS>& f, uint4 (*scr)[16][KS / 8],
+                                         f32x4 (&acc)[NA][NT]) {
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  // loaded layout -> LDS
 #pragma unroll
-  for (int i = 0; i < KS / 32; ++i)
+  for (int m = 0; m < NA; ++m)
+#pragma unroll
+    for (int j = 0; j < KS / 32; ++j) {
+      const int rho = (lane >> 3) + 8 * (j & 1), c = 8 * (j >> 1) + (lane & 7);
+      scr[m][rho][c ^ swz<KS>(rho)] = f.a[m][j];
+    }
+  // the reads below take chunks other lanes of this wave wrote: keep them
+  // after the writes (LDS executes one wave's accesses in order)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < KS / 32; ++i) {
+    uint4 a[NA];
+#pragma unroll
+    for (int m = 0; m < NA; ++m) a[m] = scr[m][r][(4 * i + q) ^ swz<KS>(r)];
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int m = 0; m < NA; ++m)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.a[m][i]),
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[m]),
                                                             __builtin_bit_cast(bf16x8, f.b[n][i]),
                                                             acc[m][n], 0, 0, 0);
+  }
+  // the next step's writes overwrite what these reads take
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // K loop of one wave over steps wave, wave+kWK, ... (double-buffered loads),
 // then the kWK partial sums are added in LDS in wave order; wave 0 returns
-// the total.  Lane (r = lane % 16, q = lane / 16) reads KS/4 contiguous
-// elements at offset q*KS/4 of its row in every step: both operands use the
-// same K order, so the MFMA sums run over the full step.
+// the total.  pa[m]: this lane's load position in weight tile m (row L / 8,
+// byte 16 (L % 8)); ld8: 8 rows, in elements; pb[n]: token row r + 8 q.
+// Both operands use the same K order, so the MFMA sums run over the full step.
 template <int NA, int NT, int KS>
 __device__ __forceinline__ void stream_k(const uint16_t* const (&pa)[NA],
-                                         const uint16_t* const (&pb)[NT], int steps,
+                                         const uint16_t* const (&pb)[NT], int64_t ld8, int steps,
                                          f32x4 (&acc)[NA][NT]) {
+  static_assert(KS == 128 || KS == 64, "K step of one or two 128-byte lines per row");
+  __shared__ uint4 scr[kWK][NA][16][KS / 8];
   __shared__ f32x4 red[kWK - 1][NA][NT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -83,12 +126,12 @@ __device__ __forceinline__ void stream_k(const uint16_t* const (&pa)[NA],
     for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   int s = wave;
   Frag<NA, NT, KS> cur, nxt;
-  if (s < steps) load_frag(cur, pa, pb, s * KS);
+  if (s < steps) load_frag(cur, pa, pb, ld8, s * KS);
 #pragma unroll 1
   while (s < steps) {
     const int sn = s + kWK;
-    if (sn < steps) load_frag(nxt, pa, pb, sn * KS);
-    mma_frag(cur, acc);
+    if (sn < steps) load_frag(nxt, pa, pb, ld8, sn * KS);
+    mma_frag(cur, scr[wave], acc);
     cur = nxt;
     s = sn;
   }
@@ -135,17 +178,18 @@ __global__ __launch_bounds__(256) void gate_up_stream_bf16(FfnArgs a) {
   const uint16_t* wg = static_cast<const uint16_t*>(sh ? a.sh_gate : a.w_gate);
   const uint16_t* wu = static_cast<const uint16_t*>(sh ? a.sh_up : a.w_up);
   const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.F * H;
-  const uint16_t* pa[2] = {wg + wofs + (f0 + r) * H + q * (KS / 4), wu + wofs + (f0 + r) * H + q * (KS / 4)};
+  const int64_t lrow = f0 + (lane >> 3), lch = 8 * (lane & 7);     // load position
+  const uint16_t* pa[2] = {wg + wofs + lrow * H + lch, wu + wofs + lrow * H + lch};
   const uint16_t* pb[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int64_t p = tl.row0 + min(16 * n + r, tl.rows - 1);
     const uint16_t* b = sh ? static_cast<const uint16_t*>(a.xs) + (p - TK) * H
                            : static_cast<const uint16_t*>(a.xr) + (a.xr_rows ? a.xr_rows[p] : p) * H;
-    pb[n] = b + q * (KS / 4);
+    pb[n] = b + q * 8;
   }
   f32x4 acc[2][NT];
-  stream_k<2, NT, KS>(pa, pb, a.H / KS, acc);
+  stream_k<2, NT, KS>(pa, pb, 8 * H, a.H / KS, acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -174,16 +218,17 @@ __global__ __launch_bounds__(256) void down_stream_bf16(FfnArgs a) {
   const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.H * a.F;
   const uint16_t* pa[NA];
 #pragma unroll
-  for (int m = 0; m < NA; ++m) pa[m] = wd + wofs + static_cast<int64_t>(h0 + 16 * m + r) * Fg + q * (KS / 4);
+  for (int m = 0; m < NA; ++m)
+    pa[m] = wd + wofs + static_cast<int64_t>(h0 + 16 * m + (lane >> 3)) * Fg + 8 * (lane & 7);
   const uint16_t* pb[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int64_t p = tl.row0 + min(16 * n + r, tl.rows - 1);
     pb[n] = (sh ? static_cast<const uint16_t*>(a.h_sh) + (p - TK) * a.Fs
-                : static_cast<const uint16_t*>(a.h) + p * a.F) + q * (KS / 4);
+                : static_cast<const uint16_t*>(a.h) + p * a.F) + q * 8;
   }
   f32x4 acc[NA][NT];
-  stream_k<NA, NT, KS>(pa, pb, Fg / KS, acc);
+  stream_k<NA, NT, KS>(pa, pb, 8 * static_cast<int64_t>(Fg), Fg / KS, acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
