@@ -16,7 +16,9 @@
 //    loop free of divergent control flow.
 // Each wave's loads for its next K step (operands and scales) are issued
 // before the current step's MFMAs, so a load's latency overlaps a step of
-// compute instead of stalling every step.
+// compute instead of stalling every step.  As in the bf16 stream, weights
+// are loaded in whole 128-byte lines with the nontemporal hint and pass
+// through a per-wave LDS scratch into the MFMA layout.
 // The SwiGLU output is written in fp32; the activation-quant kernel turns it
 // into e4m3 codes + per-128 scales for the down projection.
 #include "kernels.h"
@@ -38,9 +40,14 @@ __device__ __forceinline__ f32x4 mma_fp8(const uint4 (&a)[2], const uint4 (&b)[2
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 0, 0, 0, 127, 0, 127);
 }
 
-// One wave's operands of one K step (one 128-wide quantisation block): 32
-// bytes per lane of NA weight row-tiles and NT token sub-tiles, and their
-// scales.
+// One wave's operands of one K step (one 128-wide quantisation block) and
+// their scales.
+//  a: NA weight row-tiles of 16 rows x 128 bytes as loaded: load g covers
+//     rows 8 g + [0, 8) in whole 128-byte lines (lane L: row L / 8, 16-byte
+//     chunk L % 8), with the nontemporal hint;
+//  b: NT token sub-tiles in the MFMA layout: lane (r = L % 16, q = L / 16)
+//     holds chunks q and q + 4 of row r (the MFMA's K order, permuted the same
+//     way for the weights when they are read back from LDS).
 template <int NA, int NT>
 struct Frag8 {
   uint4 a[NA][2];
@@ -53,31 +60,55 @@ template <int NA, int NT>
 __device__ __forceinline__ void load_frag8(Frag8<NA, NT>& f, const uint8_t* const (&pa)[NA],
                                            const float* const (&wsc)[NA],
                                            const uint8_t* const (&pb)[NT],
-                                           const float* const (&bsc)[NT], int s) {
+                                           const float* const (&bsc)[NT], int64_t ld8, int s) {
   const int koff = s * 128;
 #pragma unroll
   for (int m = 0; m < NA; ++m) {
-    const uint4* p = reinterpret_cast<const uint4*>(pa[m] + koff);
-    f.a[m][0] = p[0];
-    f.a[m][1] = p[1];
+    f.a[m][0] = load_nt(reinterpret_cast<const uint4*>(pa[m] + koff));
+    f.a[m][1] = load_nt(reinterpret_cast<const uint4*>(pa[m] + ld8 + koff));
     f.ws[m] = wsc[m][s];
   }
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const uint4* p = reinterpret_cast<const uint4*>(pb[n] + koff);
     f.b[n][0] = p[0];
-    f.b[n][1] = p[1];
+    f.b[n][1] = p[4];
     f.bs[n] = bsc[n][s];
   }
 }
 
+// Per-wave LDS scratch from the loaded weight layout to the MFMA layout: row
+// rho (0..15) of tile m holds its 8 chunks, chunk c at slot c ^ ((rho >> 1)
+// & 7), which keeps the 8-row writes and the 16-row reads of one chunk free
+// of bank conflicts (rows 128 B apart pair up by parity).
 template <int NA, int NT>
-__device__ __forceinline__ void mma_frag8(const Frag8<NA, NT>& f, f32x4 (&acc)[NA][NT]) {
+__device__ __forceinline__ void mma_frag8(const Frag8<NA, NT>& f, uint4 (*scr)[16][8], f32x4 (&acc)[NA][NT]) {
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < NA; ++m)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int rho = (lane >> 3) + 8 * g;
+      scr[m][rho][(lane & 7) ^ ((rho >> 1) & 7)] = f.a[m][g];
+    }
+  // the reads take chunks other lanes of this wave wrote (LDS executes one
+  // wave's accesses in order)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+  uint4 w[NA][2];
+#pragma unroll
+  for (int m = 0; m < NA; ++m) {
+    w[m][0] = scr[m][r][q ^ ((r >> 1) & 7)];
+    w[m][1] = scr[m][r][(q + 4) ^ ((r >> 1) & 7)];
+  }
+  // the next step's writes overwrite what these reads take
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
     for (int m = 0; m < NA; ++m) {
-      const f32x4 c = mma_fp8(f.a[m], f.b[n]);
+      const f32x4 c = mma_fp8(w[m], f.b[n]);
       const float sc = f.ws[m] * f.bs[n];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(c[i], sc, acc[m][n][i]);
@@ -87,13 +118,16 @@ __device__ __forceinline__ void mma_frag8(const Frag8<NA, NT>& f, f32x4 (&acc)[N
 // One wave's K loop for NA weight row-tiles of 16 rows and NT token
 // sub-tiles (steps wave, wave + kWK, ..., the next step's loads in flight
 // during the current step's MFMAs); then the kWK partial sums are added in
-// LDS in wave order (wave 0 keeps them).
+// LDS in wave order (wave 0 keeps them).  pa[m]: this lane's load position
+// in tile m (row L / 8, byte 16 (L % 8)); ld8: 8 rows in bytes; pb[n]: token
+// row r + 16 q.
 template <int NA, int NT>
 __device__ __forceinline__ void stream_k_fp8(const uint8_t* const (&pa)[NA],
                                              const float* const (&wsc)[NA],
                                              const uint8_t* const (&pb)[NT],
-                                             const float* const (&bsc)[NT], int steps,
+                                             const float* const (&bsc)[NT], int64_t ld8, int steps,
                                              f32x4 (&acc)[NA][NT]) {
+  __shared__ uint4 scr[kWK][NA][16][8];
   __shared__ f32x4 red[kWK - 1][NA][NT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -102,12 +136,12 @@ __device__ __forceinline__ void stream_k_fp8(const uint8_t* const (&pa)[NA],
     for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   int s = wave;
   Frag8<NA, NT> cur, nxt;
-  if (s < steps) load_frag8(cur, pa, wsc, pb, bsc, s);
+  if (s < steps) load_frag8(cur, pa, wsc, pb, bsc, ld8, s);
 #pragma unroll 1
   while (s < steps) {
     const int sn = s + kWK;
-    if (sn < steps) load_frag8(nxt, pa, wsc, pb, bsc, sn);
-    mma_frag8(cur, acc);
+    if (sn < steps) load_frag8(nxt, pa, wsc, pb, bsc, ld8, sn);
+    mma_frag8(cur, scr[wave], acc);
     cur = nxt;
     s = sn;
   }
@@ -147,7 +181,8 @@ __global__ __launch_bounds__(256) void gate_up_stream_fp8(FfnArgs a) {
   const float* su = sh ? a.sh_s_up : a.s_up;
   const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.F * H;
   const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.F / 128) * KB) + (f0 / 128) * KB;
-  const uint8_t* pa[2] = {wg + wofs + (f0 + r) * H + q * 32, wu + wofs + (f0 + r) * H + q * 32};
+  const int64_t lrow = f0 + (lane >> 3), lch = 16 * (lane & 7);     // load position
+  const uint8_t* pa[2] = {wg + wofs + lrow * H + lch, wu + wofs + lrow * H + lch};
   const float* wsc[2] = {sg + sofs, su + sofs};
   const uint8_t* pb[NT];
   const float* bsc[NT];
@@ -166,11 +201,11 @@ __global__ __launch_bounds__(256) void gate_up_stream_fp8(FfnArgs a) {
       base = static_cast<const uint8_t*>(a.xr);
       sbase = a.xr_scales;
     }
-    pb[n] = base + row * H + q * 32;
+    pb[n] = base + row * H + q * 16;
     bsc[n] = sbase + row * KB;
   }
   f32x4 acc[2][NT];
-  stream_k_fp8<2>(pa, wsc, pb, bsc, static_cast<int>(KB), acc);
+  stream_k_fp8<2>(pa, wsc, pb, bsc, 8 * H, static_cast<int>(KB), acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -201,8 +236,9 @@ __global__ __launch_bounds__(256) void down_stream_fp8(FfnArgs a) {
   const float* sd = sh ? a.sh_s_down : a.s_down;
   const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.H * a.F;
   const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.H / 128) * KB) + (h0 / 128) * KB;
-  const uint8_t* pa[2] = {wd + wofs + static_cast<int64_t>(h0 + r) * Fg + q * 32,
-                          wd + wofs + static_cast<int64_t>(h0 + 16 + r) * Fg + q * 32};
+  const int lch = 16 * (lane & 7);                                   // load position
+  const uint8_t* pa[2] = {wd + wofs + static_cast<int64_t>(h0 + (lane >> 3)) * Fg + lch,
+                          wd + wofs + static_cast<int64_t>(h0 + 16 + (lane >> 3)) * Fg + lch};
   const float* wsc[2] = {sd + sofs, sd + sofs};
   const uint8_t* pb[NT];
   const float* bsc[NT];
@@ -210,15 +246,15 @@ __global__ __launch_bounds__(256) void down_stream_fp8(FfnArgs a) {
   for (int n = 0; n < NT; ++n) {
     const int64_t p = tl.row0 + min(n * 16 + r, tl.rows - 1);
     if (sh) {
-      pb[n] = static_cast<const uint8_t*>(a.hq_sh) + (p - TK) * a.Fs + q * 32;
+      pb[n] = static_cast<const uint8_t*>(a.hq_sh) + (p - TK) * a.Fs + q * 16;
       bsc[n] = a.h_sh_scales + (p - TK) * KB;
     } else {
-      pb[n] = static_cast<const uint8_t*>(a.hq) + p * a.F + q * 32;
+      pb[n] = static_cast<const uint8_t*>(a.hq) + p * a.F + q * 16;
       bsc[n] = a.h_scales + p * KB;
     }
   }
   f32x4 acc[2][NT];
-  stream_k_fp8<2>(pa, wsc, pb, bsc, static_cast<int>(KB), acc);
+  stream_k_fp8<2>(pa, wsc, pb, bsc, 8 * static_cast<int64_t>(Fg), static_cast<int>(KB), acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
