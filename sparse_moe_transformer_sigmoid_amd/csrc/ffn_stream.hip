@@ -159,11 +159,11 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, fl
 
 }  // namespace
 
-// gate_up: block = 16 intermediate features (16 gate + 16 up weight rows) of
-// one work item of up to 16*NT grouped rows.  Sub-tiles past the item's rows
-// read its last row again (in bounds, not stored), which keeps the K loop
-// free of divergent control flow.
-template <int NT>
+// gate_up: block = 16 * NF intermediate features (16 NF gate + 16 NF up
+// weight rows) of one work item of up to 16*NT grouped rows.  Sub-tiles past
+// the item's rows read its last row again (in bounds, not stored), which
+// keeps the K loop free of divergent control flow.
+template <int NT, int NF = 1>
 __global__ __launch_bounds__(256) void gate_up_stream_bf16(FfnArgs a) {
   constexpr int KS = step_k<NT>();
   const int ti = blockIdx.y;
@@ -171,15 +171,20 @@ __global__ __launch_bounds__(256) void gate_up_stream_bf16(FfnArgs a) {
   const Tile tl = a.tiles[ti];
   const bool sh = tl.group == a.E;
   const int Fg = sh ? a.Fs : a.F;
-  const int f0 = blockIdx.x * 16;
+  const int f0 = blockIdx.x * 16 * NF;
   if (f0 >= Fg) return;
   const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
   const int64_t H = a.H, TK = static_cast<int64_t>(a.T) * a.k;
   const uint16_t* wg = static_cast<const uint16_t*>(sh ? a.sh_gate : a.w_gate);
   const uint16_t* wu = static_cast<const uint16_t*>(sh ? a.sh_up : a.w_up);
   const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.F * H;
-  const int64_t lrow = f0 + (lane >> 3), lch = 8 * (lane & 7);     // load position
-  const uint16_t* pa[2] = {wg + wofs + lrow * H + lch, wu + wofs + lrow * H + lch};
+  const int64_t lrow = f0 + (lane >> 3), lch = 8 * (lane & 7);
+  const uint16_t* pa[2 * NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    pa[j] = wg + wofs + (lrow + 16 * j) * H + lch;
+    pa[NF + j] = wu + wofs + (lrow + 16 * j) * H + lch;
+  }
   const uint16_t* pb[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -188,8 +193,8 @@ __global__ __launch_bounds__(256) void gate_up_stream_bf16(FfnArgs a) {
                            : static_cast<const uint16_t*>(a.xr) + (a.xr_rows ? a.xr_rows[p] : p) * H;
     pb[n] = b + q * 8;
   }
-  f32x4 acc[2][NT];
-  stream_k<2, NT, KS>(pa, pb, 8 * H, a.H / KS, acc);
+  f32x4 acc[2 * NF][NT];
+  stream_k<2 * NF, NT, KS>(pa, pb, 8 * H, a.H / KS, acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -197,8 +202,11 @@ __global__ __launch_bounds__(256) void gate_up_stream_bf16(FfnArgs a) {
     const int64_t pr = tl.row0 + 16 * n + r;
     uint16_t* dst = sh ? static_cast<uint16_t*>(a.h_sh) + (pr - TK) * a.Fs
                        : static_cast<uint16_t*>(a.h) + pr * a.F;
-    store_bf16x4(dst + f0 + 4 * q, silu(acc[0][n][0]) * acc[1][n][0], silu(acc[0][n][1]) * acc[1][n][1],
-                 silu(acc[0][n][2]) * acc[1][n][2], silu(acc[0][n][3]) * acc[1][n][3]);
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+      store_bf16x4(dst + f0 + 16 * j + 4 * q, silu(acc[j][n][0]) * acc[NF + j][n][0],
+                   silu(acc[j][n][1]) * acc[NF + j][n][1], silu(acc[j][n][2]) * acc[NF + j][n][2],
+                   silu(acc[j][n][3]) * acc[NF + j][n][3]);
   }
 }
 
@@ -309,7 +317,9 @@ __global__ __launch_bounds__(256) void down_simple_f32(FfnArgs a) {
 hipError_t launch_gate_up_stream(const FfnArgs& a, hipStream_t st) {
   const dim3 grid(std::max(a.F, a.Fs) / 16, static_cast<unsigned>(a.tile_bound));
   switch (a.bm) {
-    case 16: hipLaunchKernelGGL(gate_up_stream_bf16<1>, grid, dim3(256), 0, st, a); break;
+    // 32 features per block for 16-row items: K2 decode gate_up 2.87 -> 2.85 ms
+    // at T=128, 3.25 -> 3.20 ms at T=256
+    case 16: hipLaunchKernelGGL((gate_up_stream_bf16<1, 2>), dim3(grid.x / 2, grid.y), dim3(256), 0, st, a); break;
     case 32: hipLaunchKernelGGL(gate_up_stream_bf16<2>, grid, dim3(256), 0, st, a); break;
     case 64: hipLaunchKernelGGL(gate_up_stream_bf16<4>, grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
@@ -370,10 +380,12 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   const int64_t rows = static_cast<int64_t>(a.T) * a.k;
   const double per_expert = static_cast<double>(rows) / a.E;
   const int stream_bm = per_expert < 6.0 ? 16 : (per_expert < 12.0 ? 32 : 64);
+  // tiled from 10 rows per expert: K2 T=384 (8 rows) streams in 5.50 ms
+  // against 5.67 tiled (fp8 2.97 against 3.10); T=512 (10.7 rows) ties
   if (weight_dtype == MOE_FP8_E4M3)
-    return per_expert >= 8.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? FfnPlan{tile_fp8_rows(), FfnPlan::kTiled}
+    return per_expert >= 10.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? FfnPlan{tile_fp8_rows(), FfnPlan::kTiled}
                                                                    : FfnPlan{stream_bm, FfnPlan::kStream};
-  if (per_expert >= 8.0 && tile_shapes_ok(a.T, a.H, a.F, a.Fs)) {
+  if (per_expert >= 10.0 && tile_shapes_ok(a.T, a.H, a.F, a.Fs)) {
     // few work items (few, fat experts: one expert-parallel rank, the dense
     // layer) split the K loop so that the grid still fills the chip
     FfnPlan p{tile_rows(), FfnPlan::kTiled};

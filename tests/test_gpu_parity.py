@@ -52,7 +52,7 @@ SMALL = [
     (W["small_bf16"].replace(name="small_bf16_e64", n_routed_experts=64), 600),
     (W["small_grouped_bf16"].replace(name="small_grouped_bf16_e64", n_routed_experts=64), 520),
     # fp8: streamed items of 16 rows (1, 7 tokens) and 32 rows (28), tiled from
-    # 8 rows per expert on; hidden size 640 does not fit the fp8 tiles, so 100
+    # 10 rows per expert on; hidden size 640 does not fit the fp8 tiles, so 100
     # tokens stream in 64-row items and 40 in 32-row items
     (W["small_fp8"], 1), (W["small_fp8"], 7), (W["small_fp8"], 28), (W["small_fp8"], 100), (W["small_fp8"], 300),
     (W["small_fp8"].replace(name="small_fp8_h640", hidden_size=640), 100),
