@@ -278,6 +278,7 @@ moe_status_t ffn_prepare(const moe_config_t* c, FfnArgs& f, int64_t T, void* ws)
   f.kind = plan.kind;
   f.ks_gu = plan.ks_gu;
   f.ks_dn = plan.ks_dn;
+  f.w_once = plan.w_once;
   f.part = at<float>(ws, L.part);
   f.tiles = at<Tile>(ws, L.tiles);
   f.tile_count = at<int32_t>(ws, L.tcount);

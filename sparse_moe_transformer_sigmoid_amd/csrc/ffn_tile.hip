@@ -60,9 +60,11 @@ __device__ __forceinline__ f32x16 mma32(const uint4& a, const uint4& b, const f3
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
-// 16 bytes per lane from global memory straight into LDS at l + 16 * lane
+// 16 bytes per lane from global memory straight into LDS at l + 16 * lane;
+// AUX 2 = the nontemporal hint
+template <int AUX>
 __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds((glb_ptr)(g), (lds_ptr)(l), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((glb_ptr)(g), (lds_ptr)(l), 16, 0, AUX);
 }
 
 }  // namespace
@@ -72,7 +74,9 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
 // `ks` > 1 splits the K loop over ks blocks (few work items): each writes its
 // fp32 partial sums to a.part, and ffn_split_finish adds them up in part
 // order and applies the epilogue.
-template <int MODE>
+// WNT: the weight DMA carries the nontemporal hint (each weight slab is
+// expected to be read by one tile only).
+template <int MODE, bool WNT>
 __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int ks) {
   // two stages as separate objects: the compiler then knows that a DMA into
   // one stage does not alias LDS reads of the other
@@ -151,10 +155,10 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
     const uint32_t ko = static_cast<uint32_t>(s) * kRowB;
     if (g < 16) {
       const int i = g >> 1, hf = g & 1;
-      dma16(wsb[hf] + (woff[i] + ko), st + (128 * wave + 64 * hf + 8 * i) * kRowB);
+      dma16<WNT ? 2 : 0>(wsb[hf] + (woff[i] + ko), st + (128 * wave + 64 * hf + 8 * i) * kRowB);
     } else {
       const int i = g - 16;
-      dma16(xsb + (xoff[i] + ko), st + (kBW + 32 * wave + 8 * i) * kRowB);
+      dma16<0>(xsb + (xoff[i] + ko), st + (kBW + 32 * wave + 8 * i) * kRowB);
     }
   };
 
@@ -400,8 +404,12 @@ static hipError_t launch_tile(const FfnArgs& a, int slabs, int ks, hipStream_t s
   // a multiple of 8: block b serves item (b % 8) * per + b / 8 with
   // per = ceil(items / 8), which needs 8 * per blocks to reach every item
   const int64_t blocks = (static_cast<int64_t>(slabs) * a.tile_bound * ks + kXcd - 1) / kXcd * kXcd;
-  hipLaunchKernelGGL((ffn_tile_bf16<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
-                     slabs, ks);
+  if (a.w_once)
+    hipLaunchKernelGGL((ffn_tile_bf16<MODE, true>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+                       slabs, ks);
+  else
+    hipLaunchKernelGGL((ffn_tile_bf16<MODE, false>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+                       slabs, ks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1) return e;
   const int64_t rows = static_cast<int64_t>(a.T) * a.k + a.T;
