@@ -382,9 +382,14 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   const int stream_bm = per_expert < 6.0 ? 16 : (per_expert < 12.0 ? 32 : 64);
   // tiled from 10 rows per expert: K2 T=384 (8 rows) streams in 5.50 ms
   // against 5.67 tiled (fp8 2.97 against 3.10); T=512 (10.7 rows) ties
-  if (weight_dtype == MOE_FP8_E4M3)
-    return per_expert >= 10.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs) ? FfnPlan{tile_fp8_rows(), FfnPlan::kTiled}
-                                                                   : FfnPlan{stream_bm, FfnPlan::kStream};
+  if (weight_dtype == MOE_FP8_E4M3) {
+    if (per_expert >= 10.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs)) {
+      FfnPlan p{tile_fp8_rows(), FfnPlan::kTiled};
+      p.w_once = per_expert <= 64.0;   // as for bf16 below (gate_up only: K2 fp8 T=512 layer 3.15 -> 3.10 ms)
+      return p;
+    }
+    return {stream_bm, FfnPlan::kStream};
+  }
   if (per_expert >= 10.0 && tile_shapes_ok(a.T, a.H, a.F, a.Fs)) {
     // few work items (few, fat experts: one expert-parallel rank, the dense
     // layer) split the K loop so that the grid still fills the chip

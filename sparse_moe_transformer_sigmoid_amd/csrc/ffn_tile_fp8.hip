@@ -36,9 +36,13 @@ constexpr int kXcd = 8;
 // loads is an explicit s_waitcnt vmcnt(n) below.  The instruction has no
 // register result (lane i writes 16 or 4 bytes at LDS address m0 + 16 i or
 // m0 + 4 i); its address operand is read at issue.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g) : "memory", "m0");
+  if (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(m0v), "v"(g) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
@@ -68,7 +72,9 @@ __device__ __forceinline__ f32x16 mma_fp8_32(const uint4& a0, const uint4& a1, c
 // (gate_up: 32 gate then 32 up rows of features o0 + 32*wm + [0, 32)) and
 // grouped rows 64*wn + [0, 64); while one wave of a SIMD applies the scales
 // of its partial products (VALU), the other's MFMAs run.
-template <int MODE>
+// WNT: the weight DMA carries the nontemporal hint (each weight slab is
+// expected to be read by one tile only)
+template <int MODE, bool WNT>
 __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
   // three stages as separate objects
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     const int64_t ko = static_cast<int64_t>(s) * kRowB;
     const uint32_t l = lds_addr(st);
     if (g < 4) {
-      dma16(wdma + g * rstride8 + ko + dch[g & 1] * 16, l + (32 * wave + 8 * g) * kRowB);
+      dma16<WNT>(wdma + g * rstride8 + ko + dch[g & 1] * 16, l + (32 * wave + 8 * g) * kRowB);
     } else if (g < 6) {
       dma16(xb[g - 4] + ko, l + (kBW + 16 * wave + 8 * (g - 4)) * kRowB);
     } else {
@@ -354,8 +360,15 @@ static hipError_t launch_tile_fp8(const FfnArgs& a, int slabs, hipStream_t st) {
   // a multiple of 8: block b serves item (b % 8) * per + b / 8 with
   // per = ceil(items / 8), which needs 8 * per blocks to reach every item
   const int64_t blocks = (static_cast<int64_t>(slabs) * a.tile_bound + kXcd - 1) / kXcd * kXcd;
-  hipLaunchKernelGGL((ffn_tile_fp8<MODE>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, a,
-                     slabs);
+  // the hint on gate_up only: on down (tile-major, 56 slabs per token tile)
+  // it cost more than it gained (K2 fp8 T=2048: layer 3.67 -> 3.75 ms with
+  // it on both, gate_up alone 2.23 -> 2.20)
+  if (a.w_once && MODE == 0)
+    hipLaunchKernelGGL((ffn_tile_fp8<MODE, true>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, a,
+                       slabs);
+  else
+    hipLaunchKernelGGL((ffn_tile_fp8<MODE, false>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, a,
+                       slabs);
   return hipGetLastError();
 }
 
