@@ -317,9 +317,16 @@ __global__ __launch_bounds__(256) void down_simple_f32(FfnArgs a) {
 hipError_t launch_gate_up_stream(const FfnArgs& a, hipStream_t st) {
   const dim3 grid(std::max(a.F, a.Fs) / 16, static_cast<unsigned>(a.tile_bound));
   switch (a.bm) {
-    // 32 features per block for 16-row items: K2 decode gate_up 2.87 -> 2.85 ms
-    // at T=128, 3.25 -> 3.20 ms at T=256
-    case 16: hipLaunchKernelGGL((gate_up_stream_bf16<1, 2>), dim3(grid.x / 2, grid.y), dim3(256), 0, st, a); break;
+    // 32 features per block for 16-row items on a large grid (K2 decode
+    // gate_up 2.87 -> 2.85 ms at T=128, 3.25 -> 3.20 ms at T=256); 16 on a
+    // small one, where fewer blocks per CU round less well (T=1 0.095 ->
+    // 0.090 ms, T=2 0.166 -> 0.158 ms with 16)
+    case 16:
+      if (a.tile_bound >= 128)
+        hipLaunchKernelGGL((gate_up_stream_bf16<1, 2>), dim3(grid.x / 2, grid.y), dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((gate_up_stream_bf16<1, 1>), grid, dim3(256), 0, st, a);
+      break;
     case 32: hipLaunchKernelGGL(gate_up_stream_bf16<2>, grid, dim3(256), 0, st, a); break;
     case 64: hipLaunchKernelGGL(gate_up_stream_bf16<4>, grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
