@@ -5,7 +5,8 @@
 // With a residual (the sub-block around the layer) the sum starts from it:
 //   out[t] = resid[t] + y_shared[t] + sum_j w[t][j] * y[inv[t*k + j]].
 // fp32 accumulation in that order, one rounding at the end; one block per
-// token, 16-byte vectors.
+// token, 16-byte vectors (a wave reads 1 KB of a row per instruction; the
+// routed and shared rows, read once, with the nontemporal hint).
 #include "kernels.h"
 
 namespace moe {
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
         }
       }
       if (ysh) {
-        uint4 v = reinterpret_cast<const uint4*>(ysh + t * a.H)[c];
+        uint4 v = load_nt(reinterpret_cast<const uint4*>(ysh + t * a.H) + c);
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -50,14 +51,23 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
           acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(w4[i] >> 16));
         }
       }
-      for (int j = 0; j < a.k; ++j) {
-        uint4 v = reinterpret_cast<const uint4*>(y + rs[j] * a.H)[c];
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        const float wj = ws[j];
+      // up to 8 routed rows' loads in flight per thread, then the sums in
+      // slot order; the rows are read once (nontemporal)
+      for (int j0 = 0; j0 < a.k; j0 += 8) {
+        uint4 v[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(w4[i] & 0xffffu)), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(w4[i] >> 16)), acc[2 * i + 1]);
+        for (int u = 0; u < 8; ++u)
+          if (j0 + u < a.k) v[u] = load_nt(reinterpret_cast<const uint4*>(y + rs[j0 + u] * a.H) + c);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (j0 + u >= a.k) break;
+          const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+          const float wj = ws[j0 + u];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(w4[i] & 0xffffu)), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(w4[i] >> 16)), acc[2 * i + 1]);
+          }
         }
       }
       uint4 o;
