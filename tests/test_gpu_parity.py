@@ -437,6 +437,64 @@ def test_layer_replays_from_a_graph(name, block):
         assert torch.equal(out, ref_out) and torch.equal(ids, ref_ids) and torch.equal(wts, ref_w)
 
 
+@pytest.mark.parametrize("name", ["k2_decode_bf16", "k2_prefill_bf16_zipf"])
+def test_full_size_graph_replay_rotating_batches(k2_weights, name):
+    """The launch configuration the benchmark times, at full size: one layer
+    call per token batch captured in its own HIP graph (shared workspace),
+    the graphs replayed in turn with eager calls in between.  Every replay
+    equals the eager call on the same batch bit for bit, and sampled rows of
+    each batch match the oracle."""
+    wl = W[name]
+    T = wl.num_tokens
+    cfg = B.MoeConfig.from_fields(wl.fields())
+    k = wl.num_experts_per_tok
+    batches = []
+    for b in range(2):
+        case = full_case(wl, k2_weights, T)
+        if b:
+            x = cases.enforce_gap(wl, gen.gen_x(wl, T, batch=b), case["router_w"].cpu(), case["router_bias"].cpu())
+            case["x"] = x.cuda()
+        batches.append(case)
+    weights = B.MoeWeights.from_tensors(batches[0])
+    ws = B.alloc_workspace(cfg, T)
+    bufs = [(torch.empty((T, wl.hidden_size), dtype=gen.torch_dtype(wl.act_dtype), device="cuda"),
+             torch.empty((T, k), dtype=torch.int32, device="cuda"),
+             torch.empty((T, k), dtype=torch.float32, device="cuda")) for _ in batches]
+
+    def call(i):
+        c = batches[i]
+        B.moe_layer_forward(cfg, weights, c["x"], c["router_w"], c["router_bias"], bufs[i][0], ws, bufs[i][1],
+                            bufs[i][2])
+
+    side = torch.cuda.Stream()
+    graphs = []
+    for i in range(2):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            call(i)
+        torch.cuda.synchronize()
+        graphs.append(g)
+    refs = [run_layer(wl, c) for c in batches]
+    for rep in range(4):
+        i = rep % 2
+        for o in bufs[i]:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        graphs[i].replay()
+        torch.cuda.synchronize()
+        run_layer(wl, batches[1 - i])   # eager work between replays
+        same = all(torch.equal(a, r) for a, r in zip(bufs[i], refs[i]))
+        say(f"  replay {rep} (batch {i}): equal={same}")
+        assert same
+    for i in range(2):
+        check_sampled(wl, batches[i], bufs[i][0], [0, T // 2, T - 1])
+
+
 @pytest.mark.parametrize("name,T", [("small_bf16", 300), ("small_bf16", 7), ("small_fp8", 100)])
 def test_concurrent_calls_on_two_streams(name, T):
     """The library keeps no state between calls beyond the caller's buffers:
