@@ -397,7 +397,11 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
     }
     return {stream_bm, FfnPlan::kStream};
   }
-  if (per_expert >= 10.0 && tile_shapes_ok(a.T, a.H, a.F, a.Fs)) {
+  // one expert (a dense layer) gives the tiled grid few items: streaming
+  // wins below 32 rows (dense T=16: 0.218 ms streamed, 0.238 tiled; T=32
+  // ties; T=64 0.294 against 0.252)
+  const double tiled_min = a.E == 1 ? 32.0 : 10.0;
+  if (per_expert >= tiled_min && tile_shapes_ok(a.T, a.H, a.F, a.Fs)) {
     // few work items (few, fat experts: one expert-parallel rank, the dense
     // layer) split the K loop so that the grid still fills the chip
     FfnPlan p{tile_rows(), FfnPlan::kTiled};
@@ -411,7 +415,8 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
     // 5.77 -> 5.48 ms, T=1024 6.17 -> 5.97, T=2048 6.51 -> 6.35).  With more
     // rows the slabs are re-read through L2 by an expert's tiles, and the
     // hint cost the T=8192 prefill 8 %.
-    p.w_once = per_expert <= 64.0;
+    // One expert (a dense layer): its row count is exact, T * k.
+    p.w_once = per_expert <= 64.0 || (a.E == 1 && rows <= 128 && a.T <= 128);
     return p;
   }
   return {stream_bm, FfnPlan::kStream};

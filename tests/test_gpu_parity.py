@@ -260,10 +260,11 @@ def test_moonlight_shape_full_size(T):
     assert err <= TOL[wl.weight_dtype]
 
 
-@pytest.mark.parametrize("T", [1, 128, 1024])
+@pytest.mark.parametrize("T", [1, 16, 32, 128, 1024])
 def test_dense_first_layer_full_size(T):
     """The dense first layer (SwiGLU 7168 -> 18432 -> 7168) as E = 1, k = 1,
-    scale 1 through the same entry point; every row compared."""
+    scale 1 through the same entry point; every row compared (streamed up to
+    31 rows, tiled from 32, with the nontemporal weight DMA up to 128)."""
     wl = W["k2_dense_layer_bf16"]
     case = small_case(wl, T)
     out, ids, w = run_layer(wl, case)
