@@ -313,22 +313,30 @@ __global__ __launch_bounds__(256) void down_simple_f32(FfnArgs a) {
   dst[o] = y;
 }
 
-// sub-tiles of 16 rows per work item: bm = 16 * NT
+// sub-tiles of 16 rows per work item: bm = 16 * NT.  32 features per block
+// (NF = 2) when that grid still has >= 3000 blocks, else 16.  Measured whole
+// layer, NF 2 against 1: K2 T=128 2.85 against 2.87 ms (gate_up), T=256
+// 3.20 against 3.25, T=300 5.18 against 5.28 ms, T=384 5.33 against 5.48,
+// Moonlight T=256 0.303 against 0.332, T=512 0.390 against 0.435; but K2
+// T=1 0.095 against 0.090 ms (gate_up) and T=2 0.166 against 0.158, where
+// the grid is a few hundred blocks.
 hipError_t launch_gate_up_stream(const FfnArgs& a, hipStream_t st) {
   const dim3 grid(std::max(a.F, a.Fs) / 16, static_cast<unsigned>(a.tile_bound));
+  const bool nf2 = static_cast<int64_t>(grid.x / 2) * a.tile_bound >= 3000;
+  const dim3 grid2(grid.x / 2, grid.y);
   switch (a.bm) {
-    // 32 features per block for 16-row items on a large grid (K2 decode
-    // gate_up 2.87 -> 2.85 ms at T=128, 3.25 -> 3.20 ms at T=256); 16 on a
-    // small one, where fewer blocks per CU round less well (T=1 0.095 ->
-    // 0.090 ms, T=2 0.166 -> 0.158 ms with 16)
     case 16:
-      if (a.tile_bound >= 128)
-        hipLaunchKernelGGL((gate_up_stream_bf16<1, 2>), dim3(grid.x / 2, grid.y), dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((gate_up_stream_bf16<1, 1>), grid, dim3(256), 0, st, a);
+      if (nf2) hipLaunchKernelGGL((gate_up_stream_bf16<1, 2>), grid2, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((gate_up_stream_bf16<1, 1>), grid, dim3(256), 0, st, a);
       break;
-    case 32: hipLaunchKernelGGL(gate_up_stream_bf16<2>, grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL(gate_up_stream_bf16<4>, grid, dim3(256), 0, st, a); break;
+    case 32:
+      if (nf2) hipLaunchKernelGGL((gate_up_stream_bf16<2, 2>), grid2, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((gate_up_stream_bf16<2, 1>), grid, dim3(256), 0, st, a);
+      break;
+    case 64:
+      if (nf2) hipLaunchKernelGGL((gate_up_stream_bf16<4, 2>), grid2, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((gate_up_stream_bf16<4, 1>), grid, dim3(256), 0, st, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -187,7 +187,7 @@ def full_route(wl, case):
                         **cases.route_kwargs(wl))
 
 
-@pytest.mark.parametrize("T", [128, 1, 8, 512])
+@pytest.mark.parametrize("T", [128, 1, 8, 384, 512])
 def test_k2_decode_full_size(k2_weights, T):
     wl = W["k2_decode_bf16"]
     case = full_case(wl, k2_weights, T)
