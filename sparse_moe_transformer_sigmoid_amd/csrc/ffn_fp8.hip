@@ -162,16 +162,16 @@ __device__ __forceinline__ void stream_k_fp8(const uint8_t* const (&pa)[NA],
 
 }  // namespace
 
-// gate_up: block = 16 intermediate features (16 gate + 16 up weight rows) of
-// one work item (<= 16 * NT grouped rows); h written in fp32.
-template <int NT>
+// gate_up: block = 16 * NF intermediate features (16 NF gate + 16 NF up
+// weight rows) of one work item (<= 16 * NT grouped rows); h written in fp32.
+template <int NT, int NF = 1>
 __global__ __launch_bounds__(256) void gate_up_stream_fp8(FfnArgs a) {
   const int ti = blockIdx.y;
   if (ti >= *a.tile_count) return;
   const Tile tl = a.tiles[ti];
   const bool sh = tl.group == a.E;
   const int Fg = sh ? a.Fs : a.F;
-  const int f0 = blockIdx.x * 16;
+  const int f0 = blockIdx.x * 16 * NF;
   if (f0 >= Fg) return;
   const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
   const int64_t H = a.H, KB = a.H / 128, TK = static_cast<int64_t>(a.T) * a.k;
@@ -180,10 +180,18 @@ __global__ __launch_bounds__(256) void gate_up_stream_fp8(FfnArgs a) {
   const float* sg = sh ? a.sh_s_gate : a.s_gate;
   const float* su = sh ? a.sh_s_up : a.s_up;
   const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.F * H;
-  const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.F / 128) * KB) + (f0 / 128) * KB;
   const int64_t lrow = f0 + (lane >> 3), lch = 16 * (lane & 7);     // load position
-  const uint8_t* pa[2] = {wg + wofs + lrow * H + lch, wu + wofs + lrow * H + lch};
-  const float* wsc[2] = {sg + sofs, su + sofs};
+  const uint8_t* pa[2 * NF];
+  const float* wsc[2 * NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    // the weight-block scale row of features f0 + 16 j (128-row blocks)
+    const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.F / 128) * KB) + ((f0 + 16 * j) / 128) * KB;
+    pa[j] = wg + wofs + (lrow + 16 * j) * H + lch;
+    pa[NF + j] = wu + wofs + (lrow + 16 * j) * H + lch;
+    wsc[j] = sg + sofs;
+    wsc[NF + j] = su + sofs;
+  }
   const uint8_t* pb[NT];
   const float* bsc[NT];
 #pragma unroll
@@ -204,20 +212,23 @@ __global__ __launch_bounds__(256) void gate_up_stream_fp8(FfnArgs a) {
     pb[n] = base + row * H + q * 16;
     bsc[n] = sbase + row * KB;
   }
-  f32x4 acc[2][NT];
-  stream_k_fp8<2>(pa, wsc, pb, bsc, 8 * H, static_cast<int>(KB), acc);
+  f32x4 acc[2 * NF][NT];
+  stream_k_fp8<2 * NF>(pa, wsc, pb, bsc, 8 * H, static_cast<int>(KB), acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     if (n * 16 + r >= tl.rows) continue;
     const int64_t pr = tl.row0 + n * 16 + r;
     float* dst = sh ? static_cast<float*>(a.h_sh) + (pr - TK) * a.Fs : static_cast<float*>(a.h) + pr * a.F;
-    float4 v;
-    v.x = silu(acc[0][n][0]) * acc[1][n][0];
-    v.y = silu(acc[0][n][1]) * acc[1][n][1];
-    v.z = silu(acc[0][n][2]) * acc[1][n][2];
-    v.w = silu(acc[0][n][3]) * acc[1][n][3];
-    *reinterpret_cast<float4*>(dst + f0 + 4 * q) = v;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      float4 v;
+      v.x = silu(acc[j][n][0]) * acc[NF + j][n][0];
+      v.y = silu(acc[j][n][1]) * acc[NF + j][n][1];
+      v.z = silu(acc[j][n][2]) * acc[NF + j][n][2];
+      v.w = silu(acc[j][n][3]) * acc[NF + j][n][3];
+      *reinterpret_cast<float4*>(dst + f0 + 16 * j + 4 * q) = v;
+    }
   }
 }
 
@@ -272,11 +283,23 @@ __global__ __launch_bounds__(256) void down_stream_fp8(FfnArgs a) {
 }
 
 hipError_t launch_gate_up_fp8(const FfnArgs& a, hipStream_t st) {
-  dim3 grid(std::max(a.F, a.Fs) / 16, static_cast<unsigned>(a.tile_bound));
+  // 32 features per block when that grid keeps >= 3000 blocks, as for bf16
+  const dim3 grid(std::max(a.F, a.Fs) / 16, static_cast<unsigned>(a.tile_bound));
+  const bool nf2 = static_cast<int64_t>(grid.x / 2) * a.tile_bound >= 3000;
+  const dim3 grid2(grid.x / 2, grid.y);
   switch (a.bm) {
-    case 16: hipLaunchKernelGGL(gate_up_stream_fp8<1>, grid, dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL(gate_up_stream_fp8<2>, grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL(gate_up_stream_fp8<4>, grid, dim3(256), 0, st, a); break;
+    case 16:
+      if (nf2) hipLaunchKernelGGL((gate_up_stream_fp8<1, 2>), grid2, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((gate_up_stream_fp8<1, 1>), grid, dim3(256), 0, st, a);
+      break;
+    case 32:
+      if (nf2) hipLaunchKernelGGL((gate_up_stream_fp8<2, 2>), grid2, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((gate_up_stream_fp8<2, 1>), grid, dim3(256), 0, st, a);
+      break;
+    case 64:
+      if (nf2) hipLaunchKernelGGL((gate_up_stream_fp8<4, 2>), grid2, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((gate_up_stream_fp8<4, 1>), grid, dim3(256), 0, st, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
