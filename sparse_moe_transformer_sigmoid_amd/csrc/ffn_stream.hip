@@ -396,9 +396,11 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   const double per_expert = static_cast<double>(rows) / a.E;
   const int stream_bm = per_expert < 6.0 ? 16 : (per_expert < 12.0 ? 32 : 64);
   // tiled from 10 rows per expert: K2 T=384 (8 rows) streams in 5.50 ms
-  // against 5.67 tiled (fp8 2.97 against 3.10); T=512 (10.7 rows) ties
+  // against 5.67 tiled; T=512 (10.7 rows) 5.29 tiled against 5.47.  fp8
+  // streams its 32-row items up to 12 rows per expert (T=512: 2.85 ms
+  // against 3.05 tiled) but not 64-row ones (T=640: 4.00 against 3.12).
   if (weight_dtype == MOE_FP8_E4M3) {
-    if (per_expert >= 10.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs)) {
+    if (per_expert >= 12.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs)) {
       FfnPlan p{tile_fp8_rows(), FfnPlan::kTiled};
       p.w_once = per_expert <= 64.0;   // as for bf16 below (gate_up only: K2 fp8 T=512 layer 3.15 -> 3.10 ms)
       return p;

@@ -51,10 +51,11 @@ SMALL = [
     # 64 experts and >= 512 tokens: the LDS-tiled router (128-token tiles, ragged tail)
     (W["small_bf16"].replace(name="small_bf16_e64", n_routed_experts=64), 600),
     (W["small_grouped_bf16"].replace(name="small_grouped_bf16_e64", n_routed_experts=64), 520),
-    # fp8: streamed items of 16 rows (1, 7 tokens) and 32 rows (28), tiled from
-    # 10 rows per expert on; hidden size 640 does not fit the fp8 tiles, so 100
+    # fp8: streamed items of 16 rows (1, 7 tokens) and 32 rows (28, 44), tiled
+    # from 12 rows per expert on; hidden size 640 does not fit the fp8 tiles, so 100
     # tokens stream in 64-row items and 40 in 32-row items
-    (W["small_fp8"], 1), (W["small_fp8"], 7), (W["small_fp8"], 28), (W["small_fp8"], 100), (W["small_fp8"], 300),
+    (W["small_fp8"], 1), (W["small_fp8"], 7), (W["small_fp8"], 28), (W["small_fp8"], 44), (W["small_fp8"], 100),
+    (W["small_fp8"], 300),
     (W["small_fp8"].replace(name="small_fp8_h640", hidden_size=640), 100),
     (W["small_fp8"].replace(name="small_fp8_h640", hidden_size=640), 40),
     (W["small_fp8"].replace(name="small_fp8_hot", bias="hot"), 200),
@@ -226,7 +227,7 @@ def k2_fp8_weights():
     return w
 
 
-@pytest.mark.parametrize("T", [4096, 1, 64])
+@pytest.mark.parametrize("T", [4096, 1, 64, 512])
 def test_k2_fp8_full_size(k2_fp8_weights, T):
     wl = W["k2_fp8"]
     case = full_case(wl, k2_fp8_weights, T)
