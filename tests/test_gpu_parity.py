@@ -40,9 +40,13 @@ SMALL = [
     (W["small_bf16"].replace(name="small_bf16_f384", moe_intermediate_size=384), 100),
     (W["small_bf16"].replace(name="small_bf16_f384", moe_intermediate_size=384), 40),
     (W["small_bf16"].replace(name="small_bf16_h640", hidden_size=640), 100),
-    # hidden size 2560 (40 K steps of 64) at 40 tokens: gate_up split over 7
+    # hidden size 2560 (40 K steps of 64) at 100 tokens: gate_up split over 7
     # K parts of 6, 6, 6, 6, 6, 6 and 4 steps
+    (W["small_bf16"].replace(name="small_bf16_h2560", hidden_size=2560), 100),
+    # tiled down with gate_up streamed over the 128-row tiles cut into 32-row
+    # (10 rows per expert) and 64-row items (16 rows per expert)
     (W["small_bf16"].replace(name="small_bf16_h2560", hidden_size=2560), 40),
+    (W["small_bf16"], 64),
     (W["small_bf16"].replace(name="small_bf16_e64", n_routed_experts=64), 1100),
     (W["small_grouped_bf16"], 100),
     (W["small_bf16"].replace(name="small_bf16_hot", bias="hot"), 300),
