@@ -13,23 +13,26 @@
 //    64 features, so SiLU * up is applied on matching accumulators;
 //  * down: a wave owns 128 output rows.
 // Both operands go global -> LDS by DMA (global_load_lds_dwordx4, no VGPR
-// staging), 64 K-elements (128 B per row) per step, two 80 KB stages (the
-// whole 160 KB LDS).  Each DMA source is a wave-uniform base in scalar
-// registers plus a 32-bit lane offset (the instruction's SADDR form), so an
-// issue costs no 64-bit vector address arithmetic.  Rows are unpadded; 16-byte slot = chunk ^ ((row >> 1)
-// & 7), because with 128-byte rows the 64 banks give bank group 8*(row%2) +
-// slot and a 128-bit read serves 16 lanes per cycle, so any 16 consecutive
-// rows land in distinct groups.  The grouped rows are gathered by the DMA
-// itself through the row -> token map.
-// A K step is 4 sub-steps of 16 K-elements (16 MFMAs each per wave); the
-// fragments of sub-step i+1 are read from LDS while sub-step i computes, and
-// the 20 DMA issues of the next step go out early, evenly among the MFMAs of
-// the first two sub-steps (a batch takes about one step's time to land at
-// full load, so late issues stall the end-of-step wait); then wait +
-// barrier.  The two stages are separate __shared__
-// objects and the step loop is unrolled by two, so the compiler can see that
-// the DMA into one stage never aliases the reads of the other and places no
-// wait for it in front of them.
+// staging, issued from inline asm with explicit waits), 64 K-elements (128 B
+// per row) per step, in two stages that fill the whole 160 KB LDS: per stage
+// the 512 weight rows as 16 m-tiles of 32 rows (4 per wave: each wave DMAs
+// and reads only its own 128 weight rows) and the 128 grouped rows.  Each DMA
+// source is a wave-uniform base in scalar registers plus a 32-bit lane
+// offset (the instruction's SADDR form).  Rows are unpadded; 16-byte slot =
+// chunk ^ ((row >> 1) & 7), because with 128-byte rows the 64 banks give bank
+// group 8*(row%2) + slot and a 128-bit read serves 16 lanes per cycle, so any
+// 16 consecutive rows land in distinct groups.  The grouped rows are gathered
+// by the DMA itself through the row -> token map.
+// A K step consumes the weights m-tile by m-tile (4 sub-steps of 16 K each,
+// the step's token fragments read during m-tile 0 and kept in registers),
+// and each freed m-tile slot takes the data of step s + 2 at once, so a
+// weight batch has 1.25 - 1.75 steps to land instead of under one; the token
+// stage of step s + 2 is refilled after the one barrier per step (after
+// m-tile 0, when every wave has read its token fragments).  Measured on the
+// prefill's routing (136 experts, 65,536 rows, standalone gate_up): 890 -
+// 897 TFLOP/s against 835 - 845 with both operands refilled a step ahead
+// (the dense 8192 x 4096 x 7168 shape, whose operands stay in L2, went from
+// 992 - 999 to 937 - 946).
 //
 // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs.  The
 // (slab, tile) pairs are numbered slab-major and cut into 8 contiguous
@@ -47,11 +50,7 @@ constexpr int kBM = 128;                      // grouped rows per work item
 constexpr int kBW = 512;                      // weight rows per slab
 constexpr int kBK = 64;                       // K elements per step
 constexpr int kRowB = 128;                    // bytes per LDS row (kBK bf16)
-constexpr int kStage = (kBW + kBM) * kRowB;   // 80 KB
 constexpr int kXcd = 8;
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef __attribute__((address_space(1))) void* glb_ptr;
 
 __device__ __forceinline__ f32x16 mma32(const uint4& a, const uint4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -60,13 +59,6 @@ __device__ __forceinline__ f32x16 mma32(const uint4& a, const uint4& b, const f3
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
-// 16 bytes per lane from global memory straight into LDS at l + 16 * lane;
-// AUX 2 = the nontemporal hint
-template <int AUX>
-__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds((glb_ptr)(g), (lds_ptr)(l), 16, 0, AUX);
-}
-
 }  // namespace
 
 // MODE 0: gate_up (K = H, slab = 256 features = 256 gate + 256 up rows)
@@ -80,8 +72,9 @@ template <int MODE, bool WNT>
 __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int ks) {
   // two stages as separate objects: the compiler then knows that a DMA into
   // one stage does not alias LDS reads of the other
-  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
+  // weights: [stage][m-tile][wave's 32 rows x 128 B]; tokens: [stage][128 rows x 128 B]
+  __shared__ __attribute__((aligned(16))) uint8_t wst[2][4][4 * 32 * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t tst[2][kBM * kRowB];
   // ---- XCD-chunked mapping of this block to (K part, slab, tile) ----
   const int ntile = *a.tile_count;
   const int total = slabs * ntile * ks;
@@ -149,17 +142,48 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
     xoff[i] = static_cast<uint32_t>(r) * static_cast<uint32_t>(ld * 2) + dch[i & 1] * 16;
   }
 
-  // DMA instruction g (0..19) of step s into stage st: 0-15 weight rows
-  // (8 groups of 8 rows x 2 halves), 16-19 grouped rows
-  auto dma = [&](int g, int s, uint8_t* st) {
+  // DMA from inline asm (the compiler neither tracks it nor waits for it:
+  // every wait is an explicit s_waitcnt below), SADDR form: wave-uniform
+  // 64-bit base in SGPRs + 32-bit lane offset; LDS destinations as byte
+  // addresses from the two LDS bases (taken once)
+  const uint32_t wlds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(&wst[0][0][0])));
+  const uint32_t tlds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(&tst[0][0])));
+  // (readfirstlane returns int: each half goes through uint32_t, or the low
+  // word would sign-extend into the high one)
+  auto sbase = [](const uint8_t* base) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+  };
+  const uint64_t wsb_s[2] = {sbase(wsb[0]), sbase(wsb[1])};
+  const uint64_t xsb_s = sbase(xsb);
+  auto dma_asm = [&](uint64_t bu, uint32_t voff, uint32_t lds, auto nt_tag) {
+    const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
+    if (decltype(nt_tag)::value)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(m0v), "v"(voff), "s"(bu) : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(voff), "s"(bu) : "memory", "m0");
+  };
+  // weight m-tile m (this wave's rows 32 m + [0, 32): 4 instructions of 8
+  // rows) of K step s into stage stg: wst[stg][m] starts at (4 stg + m) * 16 KB
+  auto dma_w = [&](int m, int s, int stg) {
     const uint32_t ko = static_cast<uint32_t>(s) * kRowB;
-    if (g < 16) {
-      const int i = g >> 1, hf = g & 1;
-      dma16<WNT ? 2 : 0>(wsb[hf] + (woff[i] + ko), st + (128 * wave + 64 * hf + 8 * i) * kRowB);
-    } else {
-      const int i = g - 16;
-      dma16<0>(xsb + (xoff[i] + ko), st + (kBW + 32 * wave + 8 * i) * kRowB);
-    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma_asm(wsb_s[m >> 1], woff[4 * (m & 1) + j] + ko,
+              wlds + (4 * stg + m) * (4 * 32 * kRowB) + (32 * wave + 8 * j) * kRowB,
+              std::integral_constant<bool, WNT>{});
+  };
+  // this wave's 32 of the 128 token rows of K step s into stage stg
+  auto dma_t = [&](int s, int stg) {
+    const uint32_t ko = static_cast<uint32_t>(s) * kRowB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma_asm(xsb_s, xoff[i] + ko, tlds + stg * (kBM * kRowB) + (32 * wave + 8 * i) * kRowB,
+              std::integral_constant<bool, false>{});
   };
 
   // this block's K steps [s0, s0 + steps): part kp of ks parts of `kper`
@@ -168,8 +192,8 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
   const int ksteps = K / kBK, kper = ((ksteps + ks - 1) / ks + 1) & ~1;
   const int s0 = kp * kper, steps = min(kper, ksteps - s0);
   const int sw = (r32 >> 1) & 7;                       // row swizzle of this lane's rows
-  const int arow = (128 * wave + r32) * kRowB;
-  const int brow = (kBW + r32) * kRowB;
+  const int arow = (32 * wave + r32) * kRowB;        // in wst[stg][m]
+  const int brow = r32 * kRowB;                      // in tst[stg]
 
   // The K loop and the epilogue for NN active 32-row groups of grouped rows
   // (NN = ceil(rows / 32)): a work list's last tile of an expert is usually
@@ -185,58 +209,82 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
 
-    // fragments of sub-step i (16 K-elements) of a step from stage st
-    auto frag = [&](const uint8_t* st, int i, uint4 (&af)[4], uint4 (&bf)[NN]) {
-      const int slot = ((kh * 4 + i) ^ sw) * 16;
+    auto slot = [&](int i) { return ((kh * 4 + i) ^ sw) * 16; };
+    // One K step s on stage STG.  Per wave, DMAs go out in the order T(s+2),
+    // W(s+2, 0..3) (tokens, then weight m-tiles) every step, so the waits are
+    // constants.  Weights are consumed m-tile by m-tile and each freed m-tile
+    // slot takes the data of step s + 2 at once; the step's token fragments
+    // are read during m-tile 0 and kept in registers.  The first fragments
+    // of step s + 1 (tokens, landed at this step's barrier; m-tile 0, which
+    // has 28 later DMAs at that point) are read during m-tile 3.
+    uint4 nb[NN], na;   // step s's first fragments, read during step s - 1
+    auto step = [&](auto stg_tag, int s) {
+      constexpr int STG = decltype(stg_tag)::value;
+      const int sn = s0 + min(s + 2, steps - 1);   // past the end: re-load the last step (never read)
+      const uint8_t* tk = tst[STG];
+      uint4 bf[4][NN], af[2];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) af[m] = *reinterpret_cast<const uint4*>(st + arow + 32 * m * kRowB + slot);
-#pragma unroll
-      for (int n = 0; n < NN; ++n) bf[n] = *reinterpret_cast<const uint4*>(st + brow + 32 * n * kRowB + slot);
-    };
-    // one K step: MFMAs on stage rd while the DMA of step sn fills stage wr;
-    // the next sub-step's fragments are read during the current sub-step
-    auto step = [&](const uint8_t* rd, uint8_t* wr, int sn) {
-      uint4 af[2][4], bf[2][NN];
-      frag(rd, 0, af[0], bf[0]);
+      for (int n = 0; n < NN; ++n) bf[0][n] = nb[n];
+      af[0] = na;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = i & 1;
-        if (i < 3) frag(rd, i + 1, af[c ^ 1], bf[c ^ 1]);
-        // the next step's 20 DMA issues: 10 in each of the first two sub-steps
-        const int d0 = i == 0 ? 0 : i == 1 ? 10 : 20;
-        const int d1 = i == 0 ? 10 : 20;
+        if (i < 3) {
 #pragma unroll
-        for (int g = d0; g < d1; ++g) dma(g, sn, wr);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int n = 0; n < NN; ++n) acc[m][n] = mma32(af[c][m], bf[c][n], acc[m][n]);
-        // among its MFMAs: the next fragments' LDS reads as early as
-        // possible, this sub-step's DMAs spread evenly
-        constexpr int nm = 4 * NN;
-        const int nd = d1 - d0, nr = i < 3 ? 4 + NN : 0, rp = (nr + nm - 1) / nm;
-#pragma unroll
-        for (int g = 0; g < nm; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-          for (int q = g * rp; q < min((g + 1) * rp, nr); ++q) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-          for (int q = g * nd / nm; q < (g + 1) * nd / nm; ++q) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          for (int n = 0; n < NN; ++n)
+            bf[i + 1][n] = *reinterpret_cast<const uint4*>(tk + brow + 32 * n * kRowB + slot(i + 1));
+          af[(i + 1) & 1] = *reinterpret_cast<const uint4*>(wst[STG][0] + arow + slot(i + 1));
         }
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 0; n < NN; ++n) acc[0][n] = mma32(af[i & 1], bf[i][n], acc[0][n]);
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      dma_t(sn, STG);
+      dma_w(0, sn, STG);
+#pragma unroll
+      for (int m = 1; m < 4; ++m) {
+        if (m == 3) {
+          // next step's first fragments: its tokens landed at the barrier
+          // above; its m-tile 0 (W(s+1, 0)) has W(s+1, 1..3), T(s+2) and
+          // W(s+2, 0..2) after it
+          asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
+#pragma unroll
+          for (int n = 0; n < NN; ++n)
+            nb[n] = *reinterpret_cast<const uint4*>(tst[STG ^ 1] + brow + 32 * n * kRowB + slot(0));
+          na = *reinterpret_cast<const uint4*>(wst[STG ^ 1][0] + arow + slot(0));
+        }
+        af[0] = *reinterpret_cast<const uint4*>(wst[STG][m] + arow + slot(0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < 3) af[(i + 1) & 1] = *reinterpret_cast<const uint4*>(wst[STG][m] + arow + slot(i + 1));
+#pragma unroll
+          for (int n = 0; n < NN; ++n) acc[m][n] = mma32(af[i & 1], bf[i][n], acc[m][n]);
+        }
+        // this wave's reads of m-tile m are done before its slot is refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        dma_w(m, sn, STG);
+      }
     };
 
+    // prologue: steps 0 and 1 into stages 0 and 1 (order T, W0..W3 each),
+    // then every wave's T(0) landed (36 later DMAs)
+    dma_t(s0, 0);
 #pragma unroll
-    for (int g = 0; g < 20; ++g) dma(g, s0, st0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    for (int m = 0; m < 4; ++m) dma_w(m, s0, 0);
+    dma_t(s0 + min(1, steps - 1), 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dma_w(m, s0 + min(1, steps - 1), 1);
+    asm volatile("s_waitcnt vmcnt(36)\n\ts_barrier" ::: "memory");
+    // step 0's first fragments (W(0, 0) has 32 later DMAs)
+    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+#pragma unroll
+    for (int n = 0; n < NN; ++n) nb[n] = *reinterpret_cast<const uint4*>(tst[0] + brow + 32 * n * kRowB + slot(0));
+    na = *reinterpret_cast<const uint4*>(wst[0][0] + arow + slot(0));
     for (int s = 0; s < steps; s += 2) {
-      step(st0, st1, s0 + s + 1);
-      step(st1, st0, s0 + min(s + 2, steps - 1));
+      step(std::integral_constant<int, 0>{}, s);
+      step(std::integral_constant<int, 1>{}, s + 1);
     }
+    // no DMA may still be writing LDS when the workgroup ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (ks > 1) {
       // ---- partial sums: row p of part kp holds gate | up (gate_up, width
       // 2 * max(F, Fs)) or the output row (down, width H), fp32 ----
