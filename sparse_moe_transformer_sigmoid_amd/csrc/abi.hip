@@ -279,13 +279,11 @@ moe_status_t ffn_prepare(const moe_config_t* c, FfnArgs& f, int64_t T, void* ws)
   f.ks_gu = plan.ks_gu;
   f.ks_dn = plan.ks_dn;
   f.w_once = plan.w_once;
-  f.gu_split = plan.gu_split;
   f.part = at<float>(ws, L.part);
   f.tiles = at<Tile>(ws, L.tiles);
   f.tile_count = at<int32_t>(ws, L.tcount);
   f.tile_bound = max_tiles(T, f.k, f.E, f.Fs > 0, bm);
   if (f.tile_bound > 65535) return fail(MOE_ERR_UNSUPPORTED, "too many tiles (%lld) for one launch", (long long)f.tile_bound);
-  if (f.tile_bound * f.gu_split > 65535) f.gu_split = 0;   // the split grid would not fit: tiled gate_up
   return MOE_OK;
 }
 

@@ -163,20 +163,12 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, fl
 // weight rows) of one work item of up to 16*NT grouped rows.  Sub-tiles past
 // the item's rows read its last row again (in bounds, not stored), which
 // keeps the K loop free of divergent control flow.
-// SPLIT > 1: the work list holds larger tiles (the tiled kernels' 128 rows),
-// each cut into SPLIT items of 16 * NT rows, item blockIdx.y % SPLIT.
-template <int NT, int NF = 1, int SPLIT = 1>
+template <int NT, int NF = 1>
 __global__ __launch_bounds__(256) void gate_up_stream_bf16(FfnArgs a) {
   constexpr int KS = step_k<NT>();
-  const int ti = blockIdx.y / SPLIT;
+  const int ti = blockIdx.y;
   if (ti >= *a.tile_count) return;
-  Tile tl = a.tiles[ti];
-  if (SPLIT > 1) {
-    const int skip = (blockIdx.y % SPLIT) * 16 * NT;
-    if (tl.rows <= skip) return;
-    tl.row0 += skip;
-    tl.rows = min(tl.rows - skip, 16 * NT);
-  }
+  const Tile tl = a.tiles[ti];
   const bool sh = tl.group == a.E;
   const int Fg = sh ? a.Fs : a.F;
   const int f0 = blockIdx.x * 16 * NF;
@@ -435,33 +427,15 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
     // hint cost the T=8192 prefill 8 %.
     // One expert (a dense layer): its row count is exact, T * k.
     p.w_once = per_expert <= 64.0 || (a.E == 1 && rows <= 128 && a.T <= 128);
-    // up to 24 rows per expert gate_up streams its weights faster than the
-    // tiled kernel (in items of 32 rows below 12, else 64); down stays tiled
-    if (a.E > 1 && per_expert < 24.0) {
-      p.gu_split = per_expert < 12.0 ? 4 : 2;
-      p.ks_gu = 1;
-    }
     return p;
   }
   return {stream_bm, FfnPlan::kStream};
 }
 
-// gate_up streamed over a tiled work list (128-row tiles cut into 32- or
-// 64-row items), NF = 2
-static hipError_t launch_gate_up_stream_split(const FfnArgs& a, hipStream_t st) {
-  const dim3 grid(std::max(a.F, a.Fs) / 32, static_cast<unsigned>(a.tile_bound * a.gu_split));
-  if (a.gu_split == 4) hipLaunchKernelGGL((gate_up_stream_bf16<2, 2, 4>), grid, dim3(256), 0, st, a);
-  else if (a.gu_split == 2) hipLaunchKernelGGL((gate_up_stream_bf16<4, 2, 2>), grid, dim3(256), 0, st, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
 hipError_t launch_gate_up(const FfnArgs& a, int act_dtype, int weight_dtype, hipStream_t st) {
   if (act_dtype == MOE_F32) return launch_simple_f32(a, true, st);
-  if (weight_dtype == MOE_BF16) {
-    if (a.kind == FfnPlan::kTiled && a.gu_split > 0) return launch_gate_up_stream_split(a, st);
+  if (weight_dtype == MOE_BF16)
     return a.kind == FfnPlan::kTiled ? launch_gate_up_tile(a, st) : launch_gate_up_stream(a, st);
-  }
   if (weight_dtype == MOE_FP8_E4M3)
     return a.kind == FfnPlan::kTiled ? launch_gate_up_tile_fp8(a, st) : launch_gate_up_fp8(a, st);
   return hipErrorNotSupported;

@@ -75,7 +75,6 @@ struct FfnArgs {
   int kind;            // FfnPlan::Kind of the kernels to launch
   int ks_gu, ks_dn;    // K parts of the tiled gate_up / down (1: no split)
   bool w_once;         // tiled bf16: each expert expected in one tile (its weights read once)
-  int gu_split;        // tiled bf16: gate_up streamed over the tiles, each cut into gu_split items (0: tiled)
   float* part;         // fp32 partial sums [ks][T*k + T][width] when a K part count > 1
   const int32_t* offsets;  // [E+1] (simple fp32 kernels)
   // weights (dtype per mode); routed [E][F][H] / [E][H][F], shared [Fs][H] / [H][Fs]
@@ -108,7 +107,6 @@ struct FfnPlan {
   int kind;
   int ks_gu = 1, ks_dn = 1;  // K parts of the tiled bf16 kernels
   bool w_once = false;      // tiled bf16: nontemporal weight DMA (weights expected read once)
-  int gu_split = 0;         // tiled bf16: stream gate_up over the tiles cut into this many items
   // bytes of fp32 partial sums the K parts need (0 without a split)
   int64_t part_bytes(int64_t T, int k, int H, int F, int Fs) const {
     const int64_t R = T * k + T, Fm = F > Fs ? F : Fs;

@@ -43,8 +43,8 @@ SMALL = [
     # hidden size 2560 (40 K steps of 64) at 100 tokens: gate_up split over 7
     # K parts of 6, 6, 6, 6, 6, 6 and 4 steps
     (W["small_bf16"].replace(name="small_bf16_h2560", hidden_size=2560), 100),
-    # tiled down with gate_up streamed over the 128-row tiles cut into 32-row
-    # (10 rows per expert) and 64-row items (16 rows per expert)
+    # the tiled kernels at 10 and 16 rows per expert (few work items: K
+    # splits of both GEMMs)
     (W["small_bf16"].replace(name="small_bf16_h2560", hidden_size=2560), 40),
     (W["small_bf16"], 64),
     (W["small_bf16"].replace(name="small_bf16_e64", n_routed_experts=64), 1100),
