@@ -395,10 +395,11 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   const int64_t rows = static_cast<int64_t>(a.T) * a.k;
   const double per_expert = static_cast<double>(rows) / a.E;
   const int stream_bm = per_expert < 6.0 ? 16 : (per_expert < 12.0 ? 32 : 64);
-  // tiled from 10 rows per expert: K2 T=384 (8 rows) streams in 5.50 ms
-  // against 5.67 tiled; T=512 (10.7 rows) 5.29 tiled against 5.47.  fp8
-  // streams its 32-row items up to 12 rows per expert (T=512: 2.85 ms
-  // against 3.05 tiled) but not 64-row ones (T=640: 4.00 against 3.12).
+  // bf16 tiled from 7 rows per expert (K2 T=384, 8 rows: 5.08 ms tiled
+  // against 5.37 streamed; T=448 5.12 against 5.45; DeepSeek-V3 T=256 3.55
+  // against 3.68).  fp8 streams its 32-row items up to 12 rows per expert
+  // (T=512: 2.85 ms against 3.05 tiled) but not 64-row ones (T=640: 4.00
+  // against 3.12).
   if (weight_dtype == MOE_FP8_E4M3) {
     if (per_expert >= 12.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs)) {
       FfnPlan p{tile_fp8_rows(), FfnPlan::kTiled};
@@ -410,7 +411,7 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   // one expert (a dense layer) gives the tiled grid few items: streaming
   // wins below 32 rows (dense T=16: 0.218 ms streamed, 0.238 tiled; T=32
   // ties; T=64 0.294 against 0.252)
-  const double tiled_min = a.E == 1 ? 32.0 : 10.0;
+  const double tiled_min = a.E == 1 ? 32.0 : 7.0;
   if (per_expert >= tiled_min && tile_shapes_ok(a.T, a.H, a.F, a.Fs)) {
     // few work items (few, fat experts: one expert-parallel rank, the dense
     // layer) split the K loop so that the grid still fills the chip

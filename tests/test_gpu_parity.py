@@ -47,6 +47,8 @@ SMALL = [
     # splits of both GEMMs)
     (W["small_bf16"].replace(name="small_bf16_h2560", hidden_size=2560), 40),
     (W["small_bf16"], 64),
+    # 6.5 rows per expert: the streamed 32-row items (tiled from 7)
+    (W["small_bf16"], 26),
     (W["small_bf16"].replace(name="small_bf16_e64", n_routed_experts=64), 1100),
     (W["small_grouped_bf16"], 100),
     (W["small_bf16"].replace(name="small_bf16_hot", bias="hot"), 300),
@@ -192,7 +194,7 @@ def full_route(wl, case):
                         **cases.route_kwargs(wl))
 
 
-@pytest.mark.parametrize("T", [128, 1, 8, 384, 512])
+@pytest.mark.parametrize("T", [128, 1, 8, 300, 384, 512])
 def test_k2_decode_full_size(k2_weights, T):
     wl = W["k2_decode_bf16"]
     case = full_case(wl, k2_weights, T)
