@@ -269,6 +269,10 @@ def graphed(step):
     with torch.cuda.graph(g, stream=side):
         step()
     torch.cuda.synchronize()
+    # the first replay of a graph also uploads it: part of the set-up, so
+    # that no timed step (with fewer warm-up steps than token batches) pays it
+    g.replay()
+    torch.cuda.synchronize()
     return g.replay
 
 
