@@ -375,21 +375,20 @@ namespace moe {
 
 // Rows per work-list tile and the kernel family of one call, from the
 // expected rows per expert r = T*k / E (the row capacity for one rank's
-// share).  Measured on MI355X over Kimi-K2 decode (T = 128..1024), the
-// DeepSeek-V3 and Moonlight shapes, expert-parallel rank shares and the dense
-// layer (whole-layer time, tiled vs streamed: T=256, r=5: 5.84 vs 5.65 ms;
-// T=512, r=11: 6.15 vs 6.84; T=1024, r=21: 6.48 vs 8.32):
-//  * bf16 from r = 8 on: the LDS-tiled MFMA kernels (128 rows x 512 weight
-//    rows per block); when that grid is small (few, fat experts) the K loop
-//    is split over up to 8 (gate_up) or 16 (down) blocks;
+// share).  The thresholds are whole-layer measurements on MI355X over
+// Kimi-K2 decode (T = 1..2048), the DeepSeek-V3 and Moonlight shapes,
+// expert-parallel rank shares and the dense layer (figures beside each rule
+// below):
+//  * bf16 from r = 7 on (32 for a single expert): the LDS-tiled MFMA
+//    kernels (128 rows x 512 weight rows per block); when that grid is small
+//    (few, fat experts) the K loop is split over up to 8 (gate_up) or 16
+//    (down) blocks;
 //  * below, or when the shapes do not fit the tiles: the weight-streaming
 //    kernels with work items of 16 rows below 6 rows per expert, 32 below 12
 //    and 64 beyond (128-row items run at half occupancy and were slower in
 //    every case);
-//  * fp8: the fp8 tiled kernel from r = 8 on as well (K2 fp8 layer, whole
-//    layer, tiled vs streamed: T=384, r=8: 3.10 vs 3.30 ms; T=512: 3.21 vs
-//    3.63; T=1024: 3.43 vs 5.28), else its streaming kernel with the same
-//    16 / 32 / 64-row work items.
+//  * fp8: the fp8 tiled kernel from r = 12 on, else its streaming kernel
+//    with the same 16 / 32 / 64-row work items.
 FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   if (act_dtype == MOE_F32) return {16, FfnPlan::kSimple};
   const int64_t rows = static_cast<int64_t>(a.T) * a.k;
