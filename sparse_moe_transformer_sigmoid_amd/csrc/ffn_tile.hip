@@ -237,9 +237,11 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
 #pragma unroll
         for (int n = 0; n < NN; ++n) acc[0][n] = mma32(af[i & 1], bf[i][n], acc[0][n]);
       }
+      __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       dma_t(sn, STG);
       dma_w(0, sn, STG);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int m = 1; m < 4; ++m) {
         if (m == 3) {
@@ -260,8 +262,11 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
           for (int n = 0; n < NN; ++n) acc[m][n] = mma32(af[i & 1], bf[i][n], acc[m][n]);
         }
         // this wave's reads of m-tile m are done before its slot is refilled
+        // (fenced, so no later fragment read is hoisted above the wait)
+        __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         dma_w(m, sn, STG);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
