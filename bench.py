@@ -14,7 +14,16 @@ the rank's own tokens per second.  For a sub-block workload (block) a step is
 one moe_block_forward (pre-MoE RMSNorm, the layer, the residual add).  Prints ONE JSON line (value = tokens/s) with:
   roofline      -- the dominant kernel (grouped gate_up GEMM): algorithmic
                    bytes or flops per launch / its mean duration, timed with
-                   HIP events the library records around that launch;
+                   HIP events the library records around that launch, as a
+                   fraction of the spec peak (frac) and of the measured
+                   ceiling (frac_measured);
+  prefill       -- (default decode run) the other half of the metric: the
+                   Zipf-skewed prefill, T = 8192, on the same resident
+                   weights, with its gate_up and down rooflines (MFMA);
+  ceilings      -- what this GPU sustains: HBM read rate of whole-line
+                   nontemporal loads, the MFMA issue rate (bf16, fp8) of a
+                   register-only loop, and hipBLASLt (torch.matmul) on the
+                   dense 8192 x 4096 x 7168 bf16 shape;
   cpu_baseline  -- the fp64 oracle timed on a bounded sample of the same
                    workload on the host cores.
 """
@@ -69,6 +78,77 @@ class Hip:
         return ms.value
 
 
+class ProbeLib:
+    """The measured-ceiling kernels (libmoe_probe.so, built beside libmoe.so)."""
+
+    def __init__(self):
+        path = os.path.join(ROOT, "sparse_moe_transformer_sigmoid_amd", "libmoe_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run `python -m sparse_moe_transformer_sigmoid_amd.build`")
+        self.lib = ctypes.CDLL(path)
+        self.lib.moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        self.lib.moe_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+
+
+def timed(fn, reps: int, warm: int = 2) -> float:
+    """Mean milliseconds of fn() over `reps` launches on the current stream."""
+    for _ in range(warm):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def measure_ceilings():
+    """Measured peaks of this GPU (see ProbeLib): HBM read GB/s, MFMA TFLOP/s
+    of a register-only loop (bf16 32x32x16, fp8 32x32x64 block-scaled), and
+    hipBLASLt's bf16 GEMM (torch.matmul) on 8192 x 4096 x 7168."""
+    p = ProbeLib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes, blocks = 4 << 30, 2048
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(blocks * 16, dtype=torch.uint8, device="cuda")
+
+    def read():
+        assert p.lib.moe_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, blocks,
+                                    ctypes.c_void_p(sink.data_ptr()), st) == 0
+    read_ms = timed(read, 5)
+    del buf
+    fsink = torch.empty(4096, dtype=torch.float32, device="cuda")
+    out = {"hbm_read_gbs": round(nbytes / (read_ms * 1e-3) / 1e9, 1)}
+    for fp8, iters, name in ((0, 64, "mfma_bf16_loop_tflops"), (1, 32, "mfma_fp8_loop_tflops")):
+        def mfma(fp8=fp8, iters=iters):
+            assert p.lib.moe_probe_mfma(fp8, 2048, iters, ctypes.c_void_p(fsink.data_ptr()), st) == 0
+        ms = timed(mfma, 5)
+        flops = 2048 * 4 * iters * 4 * 2 * 32 * 32 * (64 if fp8 else 16)
+        out[name] = round(flops / (ms * 1e-3) / 1e12, 1)
+    a = torch.randn(8192, 7168, device="cuda").to(torch.bfloat16)
+    b = torch.randn(7168, 4096, device="cuda").to(torch.bfloat16)
+    ms = timed(lambda: torch.mm(a, b), 20, warm=3)
+    out["hipblaslt_bf16_tflops_8192x4096x7168"] = round(2 * 8192 * 4096 * 7168 / (ms * 1e-3) / 1e12, 1)
+    out["how"] = ("4 GiB read by 2048 blocks, 16-byte nontemporal loads (1 KB per wave instruction), 8 in flight; "
+                  "2048 x 4 waves of 4 independent MFMA chains; torch.mm on resident bf16 operands; hipEvent means")
+    return out
+
+
+def with_measured(rl: dict, ceilings) -> dict:
+    """Adds the fraction of the measured ceiling of the roofline's bound."""
+    if not ceilings:
+        return rl
+    if rl["bound"] == "hbm":
+        peak = ceilings["hbm_read_gbs"]
+    else:
+        peak = ceilings["mfma_fp8_loop_tflops" if rl["peak"] == PEAK_TFLOPS[gen.FP8] else "mfma_bf16_loop_tflops"]
+    return {**rl, "peak_measured": peak, "frac_measured": round(rl["achieved"] / peak, 4)}
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -100,16 +180,19 @@ def weight_bytes_per_expert_gate_up(wl: gen.Workload, F: int) -> int:
     return 2 * F * H * (4 if wl.weight_dtype == gen.F32 else 2)
 
 
-def roofline(wl: gen.Workload, T: int, n_active: int, gate_up_ms: float, traffic, routed_rows=None):
-    """Algorithmic work of one gate_up launch against the bound it sits on:
-    the weights of the active and the shared experts once (bytes), and
-    2 * 2 * rows * H * F for the gate and up products (flops)."""
+def roofline(wl: gen.Workload, T: int, n_active: int, gate_up_ms: float, traffic, routed_rows=None,
+             kernel: str = "gate_up"):
+    """Algorithmic work of one gate_up (or down) launch against the bound it
+    sits on: the weights of the active and the shared experts once (bytes),
+    and 2 * 2 * rows * H * F for the gate and up products (down: 2 * rows *
+    H * F) (flops)."""
     F, Fs, H, k = wl.moe_intermediate_size, wl.shared_intermediate_size, wl.hidden_size, wl.num_experts_per_tok
     rows = T * k if routed_rows is None else routed_rows
-    bytes_ = round(n_active * weight_bytes_per_expert_gate_up(wl, F))
+    part = 1.0 if kernel == "gate_up" else 0.5
+    bytes_ = round(n_active * weight_bytes_per_expert_gate_up(wl, F) * part)
     if Fs:
-        bytes_ += weight_bytes_per_expert_gate_up(wl, Fs)
-    flops = 4.0 * (rows * F + T * Fs) * H
+        bytes_ += round(weight_bytes_per_expert_gate_up(wl, Fs) * part)
+    flops = 4.0 * part * (rows * F + T * Fs) * H
     peak_tf = PEAK_TFLOPS[wl.weight_dtype]
     ridge = peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
     sec = gate_up_ms * 1e-3
@@ -117,11 +200,11 @@ def roofline(wl: gen.Workload, T: int, n_active: int, gate_up_ms: float, traffic
         ach = flops / sec / 1e12
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": round(ach / peak_tf, 4), "traffic": traffic,
-                "kernel": "gate_up", "kernel_ms": round(gate_up_ms, 4), "algorithmic_flops": flops}
+                "kernel": kernel, "kernel_ms": round(gate_up_ms, 4), "algorithmic_flops": flops}
     ach = bytes_ / sec / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": "gate_up", "kernel_ms": round(gate_up_ms, 4), "algorithmic_bytes": bytes_}
+            "kernel": kernel, "kernel_ms": round(gate_up_ms, 4), "algorithmic_bytes": bytes_}
 
 
 def source_hash(name: str) -> str:
@@ -277,6 +360,7 @@ def graphed(step):
 
 
 GRAPH = False
+LAST_DOWN_MS = None   # mean down-GEMM launch of the last measure()
 
 
 def measure(cfg, weights, wl, case, T, steps, warmup, hip, factory=make_step):
@@ -298,19 +382,24 @@ def measure(cfg, weights, wl, case, T, steps, warmup, hip, factory=make_step):
     flush.fill_(1)
     torch.cuda.synchronize()
     del flush
+    evd = [(hip.event(), hip.event()) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         if not GRAPH:
             B.moe_profile_arm(B.MOE_KID_GATE_UP, *evs[i])
+            B.moe_profile_arm(B.MOE_KID_DOWN, *evd[i])
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if GRAPH:
         for i in range(steps):
             B.moe_profile_arm(B.MOE_KID_GATE_UP, *evs[i])
+            B.moe_profile_arm(B.MOE_KID_DOWN, *evd[i])
             eager()
         torch.cuda.synchronize()
     gate_up_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))  # every eager step launches it
+    global LAST_DOWN_MS
+    LAST_DOWN_MS = float(np.mean([hip.elapsed_ms(a, b) for a, b in evd]))
     n_active = None
     if ids is not None:
         for f in fns:   # every batch once more, so that each one's ids are there
@@ -366,13 +455,53 @@ def sweep(args, wl, case, cfg, weights, hip):
         _, _, wall, gu_ms, n_act = measure(cfg, weights, wl, c, T, args.steps, args.warmup, hip)
         ms = wall * 1e3 / args.steps
         by = layer_bytes(wl, T, n_act)
+        lr = layer_roofline(wl, T, n_act, ms)
         rec = {"workload": wl.name, "num_tokens": T, "ms_per_step": round(ms, 4),
                "tokens_per_s": round(T / ms * 1e3, 1), "active_experts": n_act,
                "layer_bytes": by, "layer_hbm_frac": round(by / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
-               "gate_up_ms": round(gu_ms, 4)}
+               "layer_mfma_frac": lr["mfma_frac"], "binding": lr["binding"],
+               "gate_up_ms": round(gu_ms, 4), "down_ms": round(LAST_DOWN_MS, 4),
+               "gate_up_roofline": roofline(wl, T, n_act, gu_ms, None),
+               "down_roofline": roofline(wl, T, n_act, LAST_DOWN_MS, None, kernel="down")}
         print(f"[sweep] {json.dumps(rec)}", file=sys.stderr)
         recs.append(rec)
     return recs
+
+
+PREFILL = "k2_prefill_bf16_zipf"
+
+
+def prefill_leg(case, steps, warmup, hip, ceilings):
+    """The prefill half of the metric on the decode run's resident weights:
+    the Zipf-skewed K2 layer at T = 8192 (same expert and router weights;
+    its own bias and 4 token batches), graph-replayed as the decode line."""
+    wl = gen.WORKLOADS[PREFILL]
+    dec = gen.WORKLOADS["k2_decode_bf16"]
+    same = ("hidden_size", "moe_intermediate_size", "n_routed_experts", "n_shared_experts", "weight_dtype",
+            "act_dtype", "weight_std", "seed")
+    assert all(getattr(wl, f) == getattr(dec, f) for f in same), "prefill needs the decode run's weights"
+    T = wl.num_tokens
+    c = {k: v for k, v in case.items() if k not in ("x", "xs", "router_bias")}
+    c["xs"] = [gen.gen_x(wl, T, b).cuda() for b in range(X_BATCHES)]
+    c["x"] = c["xs"][0]
+    c["router_bias"] = gen.gen_bias(wl).cuda()
+    cfg = B.MoeConfig.from_fields(wl.fields())
+    weights = B.MoeWeights.from_tensors(c)
+    _, timed_step, wall, gu_ms, n_act = measure(cfg, weights, wl, c, T, steps, warmup, hip)
+    dn_ms = LAST_DOWN_MS
+    ms = wall * 1e3 / steps
+    singles = [timed(timed_step, 1, warm=0) for _ in range(10)]
+    rec = {"workload": wl.name, "num_tokens": T, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+           "tokens_per_s": round(T * steps / wall, 1), "active_experts": n_act,
+           "roofline": with_measured(roofline(wl, T, n_act, gu_ms, stored_traffic(PREFILL, T)), ceilings),
+           "down_roofline": with_measured(roofline(wl, T, n_act, dn_ms, None, kernel="down"), ceilings),
+           "layer_roofline": layer_roofline(wl, T, n_act, ms),
+           "step_ms_p10_p50_p90": [round(float(np.percentile(singles, q)), 4) for q in (10, 50, 90)]}
+    if ceilings:
+        rec["layer_roofline"]["mfma_frac_measured"] = round(
+            layer_flops(wl, T) / (ms * 1e-3) / 1e12 / ceilings["mfma_bf16_loop_tflops"], 4)
+    del c
+    return rec
 
 
 def main():
@@ -392,6 +521,11 @@ def main():
                     help="launch every step from the host instead of replaying one captured HIP graph")
     ap.add_argument("--sweep-tokens", default=None,
                     help="comma-separated token counts measured after the main line (stderr / --extra-out)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill (T=8192, Zipf) object of the default decode run")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes")
+    ap.add_argument("--ceilings-only", action="store_true", help="print the measured ceilings and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -402,12 +536,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.ceilings_only:
+        print(json.dumps({"ceilings": measure_ceilings()}))
+        return
     wl = gen.WORKLOADS[args.workload]
     T = args.tokens or wl.num_tokens
     global GRAPH
     GRAPH = not args.eager
     B.load()
     hip = Hip()
+    ceilings = None if args.no_ceilings else measure_ceilings()
+    torch.cuda.empty_cache()
     rank = wl.ep_size > 1
     routed_rows = None
     if rank:
@@ -453,7 +592,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    rl = roofline(wl, T, n_active, gate_up_ms, stored_traffic(args.workload, T), routed_rows)
+    down_ms = LAST_DOWN_MS
+    rl = with_measured(roofline(wl, T, n_active, gate_up_ms, stored_traffic(args.workload, T), routed_rows),
+                       ceilings)
     # spread of 20 single steps after the timed region, launched as the timed
     # ones were (the timed figure is the mean over exactly `steps` back-to-back steps)
     singles = []
@@ -476,9 +617,17 @@ def main():
                    "parallelism": "none (one GPU, all experts resident)",
                    "launch": "eager" if args.eager else "hip graph replay (one captured layer step per token batch)"},
         "roofline": rl,
+        "down_roofline": with_measured(roofline(wl, T, n_active, down_ms, None, routed_rows, kernel="down"),
+                                       ceilings),
         "layer_roofline": layer_roofline(wl, T, n_active, ms_per_step, routed_rows),
         "step_ms_p10_p50_p90": [round(float(np.percentile(singles, q)), 4) for q in (10, 50, 90)],
     }
+    if ceilings:
+        lr = res["layer_roofline"]
+        lr["hbm_frac_measured"] = round(lr["bytes"] / (ms_per_step * 1e-3) / 1e9 / ceilings["hbm_read_gbs"], 4)
+        res["ceilings"] = ceilings
+    if args.workload == "k2_decode_bf16" and not args.tokens and not args.no_prefill:
+        res["prefill"] = prefill_leg(case, args.prefill_steps, min(args.warmup, 3), hip, ceilings)
     if rank:
         res["config"].update(parallelism=f"one rank of ep{wl.ep_size} (its expert FFN share only)",
                              global_experts=wl.n_routed_experts * wl.ep_size, dispatched_rows=routed_rows,

@@ -83,7 +83,8 @@ typedef struct {
 } moe_weights_t;
 
 /* Bytes of workspace every entry point below needs for T tokens (the maximum
- * over the entry points, so one workspace serves all of them). */
+ * over the entry points, so one workspace serves all of them); 0 for an
+ * invalid configuration or a token count outside 0..65536. */
 size_t moe_workspace_size(const moe_config_t* cfg, int64_t num_tokens);
 
 /* Router ("Kimi K2 Base"/"Kimi K2 0905" raw config fields: scoring_func
@@ -94,23 +95,37 @@ size_t moe_workspace_size(const moe_config_t* cfg, int64_t num_tokens);
  *   with the largest sum-of-two-best sel stay eligible;
  *   topk_ids = the k largest sel (ties: lower id), written ascending;
  *   topk_weights = s[ids] / sum(s[ids]) (if norm_topk_prob) * routed_scaling_factor.
+ * Every token gets k distinct ids in [0, E), whatever its values: a NaN sel
+ * (from NaN or infinite inputs) orders as -inf, and experts that are not
+ * eligible (groups not kept) are taken, lowest id first, only when fewer than
+ * k eligible experts with a finite sel remain.
  * x [T][H] act_dtype; router_w [E][H] act_dtype; router_bias [E] fp32;
  * topk_ids [T][k] int32; topk_weights [T][k] fp32. */
 moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* router_w,
                        const float* router_bias, int64_t num_tokens, int32_t* topk_ids,
                        float* topk_weights, void* ws, size_t ws_bytes, void* stream);
 
-/* Grouping of the T*k (token, slot) pairs by expert, stable in token order.
+/* Grouping of the T*k (token, slot) pairs by expert: the stable sort of the
+ * pairs by expert id, in flat order t*k + j inside a segment.
  *   expert_offsets [E+1]: segment of expert e is [offsets[e], offsets[e+1]),
- *     offsets[E] = T*k;
- *   sorted_token_ids [T*k]: token of each grouped row, ascending inside a segment;
- *   inv_perm [T*k]: inv_perm[t*k+j] = grouped row of (t, j);
+ *     offsets[E] = the number of grouped pairs (T*k when every id is valid);
+ *   sorted_token_ids [T*k]: token of each grouped row, ascending inside a
+ *     segment; entries from offsets[E] on are left untouched;
+ *   inv_perm [T*k]: inv_perm[t*k+j] = grouped row of (t, j), or -1;
  *   x_perm [T*k][H]: x[sorted_token_ids[p]]; act_dtype, or for FP8 weights the
  *     e4m3 codes (1 byte each) of the dynamically quantised row, with
  *   x_perm_scales [T*k][H/128] fp32 (FP8 only, else may be NULL): per token and
  *     128 channels s = amax/448 (1 if all zero), code = e4m3(RNE, saturating)(x/s)
  *     ("Kimi K2 . Down projection", quantization_config: activation_scheme dynamic).
- * x_perm may be NULL (then only the index arrays are produced). */
+ * x_perm may be NULL (then only the index arrays are produced); its rows
+ * from offsets[E] on are left untouched.
+ * topk_ids may hold any int32 values.  moe_route writes k distinct ids in
+ * [0, E) per token; other callers may not:
+ *   - a pair whose id lies outside [0, E) (for instance an expert another
+ *     expert-parallel rank holds) is not grouped: it is not counted, takes no
+ *     row, and its inv_perm entry is -1;
+ *   - a token may name one expert in several slots: each such pair is a row
+ *     of its own, in slot order. */
 moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* topk_ids,
                          int64_t num_tokens, int32_t* expert_offsets, int32_t* sorted_token_ids,
                          int32_t* inv_perm, void* x_perm, float* x_perm_scales, void* ws,
@@ -145,6 +160,8 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, const moe_weights_t* w, con
 /* Weighted combine with the shared-expert add:
  *   out[t] = y_shared[t] + sum_{j<k} topk_weights[t][j] * y_perm[inv_perm[t*k+j]],
  * accumulated in fp32 in slot order, rounded once to act_dtype (nearest even).
+ * A slot whose inv_perm entry lies outside [0, T*k) (a pair moe_permute did
+ * not group: -1) contributes nothing.
  * y_shared may be NULL when n_shared_experts == 0.  out [T][H] act_dtype. */
 moe_status_t moe_combine(const moe_config_t* cfg, const void* y_perm, const void* y_shared,
                          const float* topk_weights, const int32_t* inv_perm, int64_t num_tokens,
@@ -176,15 +193,51 @@ moe_status_t moe_block_forward(const moe_config_t* cfg, const moe_weights_t* w, 
                                int32_t* topk_ids_out, float* topk_weights_out, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* Where an intermediate of the last call lies in the caller's workspace, for
+ * inspecting it afterwards (the layout depends only on cfg and num_tokens):
+ * *offset and *bytes of region `region` (MOE_WS_*) for T tokens.  Contents
+ * after moe_expert_ffn / moe_layer_forward / moe_block_forward on that
+ * workspace ("Kimi K2 . Down projection": h = act_fn(gate_proj(x)) *
+ * up_proj(x) is the input of down_proj):
+ *   MOE_WS_H            [T*k][F] routed SwiGLU output h, act_dtype (with FP8
+ *                       weights: unspecified);
+ *   MOE_WS_H_CODES      [T*k][F] e4m3 codes of h (FP8 weights), quantised per
+ *                       row and 128 channels as x is (quantization_config:
+ *                       activation_scheme dynamic);
+ *   MOE_WS_H_SCALES     [T*k][F/128] fp32 scales of those codes;
+ *   MOE_WS_H_SHARED, MOE_WS_H_SHARED_CODES, MOE_WS_H_SHARED_SCALES: the same
+ *                       for the shared expert, [T][Fs], [T][Fs/128];
+ *   MOE_WS_Y, MOE_WS_Y_SHARED: [T*k][H] and [T][H] down outputs, act_dtype
+ *                       (moe_layer_forward / moe_block_forward only;
+ *                       moe_expert_ffn writes them to its y_perm / y_shared).
+ * Rows are the grouped rows of the call's expert_offsets.  Regions that the
+ * configuration does not use have 0 bytes.  Returns MOE_ERR_INVALID_ARG for a
+ * bad configuration, token count, region or NULL output pointer. */
+enum {
+  MOE_WS_H = 0,
+  MOE_WS_H_CODES = 1,
+  MOE_WS_H_SCALES = 2,
+  MOE_WS_H_SHARED = 3,
+  MOE_WS_H_SHARED_CODES = 4,
+  MOE_WS_H_SHARED_SCALES = 5,
+  MOE_WS_Y = 6,
+  MOE_WS_Y_SHARED = 7,
+  MOE_WS_COUNT = 8
+};
+moe_status_t moe_workspace_region(const moe_config_t* cfg, int64_t num_tokens, int32_t region,
+                                  size_t* offset, size_t* bytes);
+
 const char* moe_status_string(moe_status_t status);
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* moe_last_error(void);
 int moe_abi_version(void);
 
 /* Profiling aid.  Arms a one-shot pair of HIP events (hipEvent_t passed as
- * void*) that the next launch of kernel `kernel_id` (MOE_KID_*) on any
- * stream records around itself; NULL/NULL disarms.  Host-side state shared by
- * all threads: only for single-threaded benchmarking. */
+ * void*) that the next launch of kernel `kernel_id` (MOE_KID_*) made by a
+ * library call on the calling thread records around itself, on that call's
+ * stream; NULL/NULL disarms.  The arming is per thread.  A launch into a
+ * stream that is being captured into a HIP graph records nothing and leaves
+ * the events armed. */
 enum {
   MOE_KID_ROUTER_LOGITS = 0, /* x W_r^T                                        */
   MOE_KID_ROUTER_TOPK = 1,   /* sigmoid, bias, groups, top-k, weights          */

@@ -145,9 +145,15 @@ def act_quant(v: np.ndarray, block: int = 128) -> Tuple[np.ndarray, np.ndarray, 
 
 
 def dequant_weight(q_codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
-    """Block-quantised weight [O][I] (e4m3 codes, fp32 scales [O/b][I/b]) -> fp64."""
-    w = e4m3_decode(q_codes)
-    return w * np.repeat(np.repeat(np.asarray(scales, np.float64), block, 0), block, 1)
+    """Block-quantised weight [O][I] (e4m3 codes, fp32 scales [O/b][I/b]) -> fp64:
+    code value times its block's scale.  (The code values come from a
+    256-entry table of e4m3_decode, which is e4m3_decode of each code.)"""
+    table = e4m3_decode(np.arange(256, dtype=np.uint8))
+    q = np.asarray(q_codes, dtype=np.uint8)
+    O, I = q.shape
+    w = table[q].reshape(O // block, block, I // block, block)
+    s = np.asarray(scales, np.float64)[:, None, :, None]
+    return (w * s).reshape(O, I)
 
 
 # --------------------------------------------------------------------------
@@ -227,20 +233,44 @@ def group_gap(r: Route, n_group: int, topk_group: int) -> np.ndarray:
 # grouping tokens by expert (stable)
 # --------------------------------------------------------------------------
 def permute(ids: np.ndarray, n_experts: int):
-    """(offsets [E+1], sorted_token_ids [T*k], inv_perm [T*k]).
+    """(offsets [E+1], sorted_token_ids [n], inv_perm [T*k]).
 
     Entry (t, j) goes to segment ids[t, j]; inside a segment entries keep
-    ascending flat order t*k + j (so ascending t, as ids of a token are
-    distinct); inv_perm[t*k+j] is its row in the grouped order.
+    ascending flat order t*k + j (ascending t; a token that names one expert
+    twice keeps its slots in order); inv_perm[t*k+j] is its row in the grouped
+    order.  An entry whose id lies outside [0, E) is not grouped (no row,
+    inv_perm -1), so offsets[E] = n, the number of grouped entries (T*k when
+    every id is valid).  (The pages route every token to k of the E experts;
+    the out-of-range case is a reading for ids from other sources, e.g. an
+    expert held by another expert-parallel rank.)
     """
     T, k = ids.shape
-    flat = ids.reshape(-1)
-    counts = np.bincount(flat, minlength=n_experts)
+    flat = np.asarray(ids, np.int64).reshape(-1)
+    valid = (flat >= 0) & (flat < n_experts)
+    counts = np.bincount(flat[valid], minlength=n_experts)
     offsets = np.concatenate([[0], np.cumsum(counts)])
-    order = np.argsort(flat, kind="stable")
-    inv = np.empty_like(order)
-    inv[order] = np.arange(T * k)
-    return offsets.astype(np.int64), (order // k).astype(np.int64), inv.astype(np.int64)
+    order = np.flatnonzero(valid)[np.argsort(flat[valid], kind="stable")]
+    inv = np.full(T * k, -1, np.int64)
+    inv[order] = np.arange(len(order))
+    return offsets.astype(np.int64), (order // k).astype(np.int64), inv
+
+
+def combine(y_perm, y_shared, weights, inv_perm) -> np.ndarray:
+    """out[t] = y_shared[t] + sum_j weights[t, j] * y_perm[inv_perm[t*k + j]]
+    (step 8 above, on grouped expert outputs), skipping entries whose row
+    lies outside y_perm's T*k rows (not grouped: -1).  y_shared may be None
+    (no shared expert)."""
+    w = np.asarray(weights, np.float64)
+    T, k = w.shape
+    y = np.asarray(y_perm, np.float64)
+    out = np.zeros((T, y.shape[1])) if y_shared is None else np.array(y_shared, np.float64)
+    inv = np.asarray(inv_perm, np.int64).reshape(T, k)
+    for t in range(T):
+        for j in range(k):
+            r = inv[t, j]
+            if 0 <= r < T * k:
+                out[t] += w[t, j] * y[r]
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -250,14 +280,20 @@ def silu(z):
     return z * sigmoid(z)
 
 
-def swiglu_expert(x, w_gate, w_up, w_down, fp8_act: bool = False) -> np.ndarray:
-    """y = W_down (silu(W_gate x) * (W_up x)); rows of x are tokens; [out][in]."""
+def swiglu_hidden(x, w_gate, w_up, fp8_act: bool = False) -> np.ndarray:
+    """h = silu(W_gate x) * (W_up x), the input of the down projection (before
+    its fp8 quantisation); rows of x are tokens; [out][in]."""
     a = np.asarray(x, np.float64)
     if fp8_act:
         a = act_quant(a)[0]
     g = a @ np.asarray(w_gate, np.float64).T
     u = a @ np.asarray(w_up, np.float64).T
-    h = silu(g) * u
+    return silu(g) * u
+
+
+def swiglu_expert(x, w_gate, w_up, w_down, fp8_act: bool = False) -> np.ndarray:
+    """y = W_down (silu(W_gate x) * (W_up x)); rows of x are tokens; [out][in]."""
+    h = swiglu_hidden(x, w_gate, w_up, fp8_act)
     if fp8_act:
         h = act_quant(h)[0]
     return h @ np.asarray(w_down, np.float64).T

@@ -22,6 +22,9 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 (MOE_KID_ROUTER_LOGITS, MOE_KID_ROUTER_TOPK, MOE_KID_PERMUTE, MOE_KID_TILES, MOE_KID_GATHER,
  MOE_KID_ACT_QUANT, MOE_KID_GATE_UP, MOE_KID_DOWN, MOE_KID_COMBINE, MOE_KID_NORM, MOE_KID_COUNT) = range(11)
 
+(MOE_WS_H, MOE_WS_H_CODES, MOE_WS_H_SCALES, MOE_WS_H_SHARED, MOE_WS_H_SHARED_CODES, MOE_WS_H_SHARED_SCALES,
+ MOE_WS_Y, MOE_WS_Y_SHARED, MOE_WS_COUNT) = range(9)
+
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
 
 
@@ -101,6 +104,7 @@ def load() -> ctypes.CDLL:
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (ctypes.c_int, []),
         "moe_profile_arm": (st, [ctypes.c_int32, _P, _P]),
+        "moe_workspace_region": (st, [CP, i64, ctypes.c_int32, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -190,6 +194,27 @@ def moe_profile_arm(kernel_id: int, ev_start: Optional[int] = None, ev_stop: Opt
     """Arm a one-shot pair of raw hipEvent_t handles (ints) around the next
     launch of kernel `kernel_id` (MOE_KID_*); None/None disarms."""
     _check(load().moe_profile_arm(int(kernel_id), ev_start, ev_stop), "moe_profile_arm")
+
+
+def moe_workspace_region(cfg: MoeConfig, num_tokens: int, region: int):
+    """(byte offset, bytes) of workspace region `region` (MOE_WS_*) for num_tokens."""
+    off, n = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().moe_workspace_region(ctypes.byref(cfg), int(num_tokens), int(region), ctypes.byref(off),
+                                       ctypes.byref(n)), "moe_workspace_region")
+    return off.value, n.value
+
+
+def workspace_view(ws: torch.Tensor, cfg: MoeConfig, num_tokens: int, region: int, dtype: torch.dtype,
+                   shape) -> torch.Tensor:
+    """A tensor view of one workspace region (no copy)."""
+    off, n = moe_workspace_region(cfg, num_tokens, region)
+    esz = torch.empty((), dtype=dtype).element_size()
+    count = 1
+    for d in shape:
+        count *= d
+    if count * esz > n:
+        raise ValueError(f"region {region} holds {n} bytes, {count * esz} asked for")
+    return ws[off:off + count * esz].view(dtype).view(*shape)
 
 
 def moe_status_string(status: int) -> str:

@@ -13,7 +13,8 @@ using namespace moe;
 namespace {
 
 thread_local std::string g_err;
-hipEvent_t g_ev[MOE_KID_COUNT][2] = {};
+// profiling events armed by moe_profile_arm on this thread (one-shot)
+thread_local hipEvent_t g_ev[MOE_KID_COUNT][2] = {};
 
 constexpr int64_t kMaxTokens = 65536;
 
@@ -29,18 +30,23 @@ moe_status_t fail(moe_status_t s, const char* fmt, ...) {
 }
 
 // records the armed start event (if any) of kernel `kid` before its launch
-// and the stop event after it; one-shot
+// and the stop event after it; one-shot.  A launch into a stream that is being
+// captured into a graph records nothing and leaves the events armed.
 struct Probe {
   int kid;
   hipStream_t st;
+  bool on = false;
   Probe(int k, hipStream_t s) : kid(k), st(s) {
-    if (g_ev[kid][0]) hipEventRecord(g_ev[kid][0], st);
+    if (!g_ev[kid][0]) return;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+    on = true;
+    hipEventRecord(g_ev[kid][0], st);
   }
   ~Probe() {
-    if (g_ev[kid][1]) {
-      hipEventRecord(g_ev[kid][1], st);
-      g_ev[kid][0] = g_ev[kid][1] = nullptr;
-    }
+    if (!on) return;
+    hipEventRecord(g_ev[kid][1], st);
+    g_ev[kid][0] = g_ev[kid][1] = nullptr;
   }
 };
 
@@ -422,8 +428,37 @@ const char* moe_status_string(moe_status_t s) {
 const char* moe_last_error(void) { return g_err.c_str(); }
 
 size_t moe_workspace_size(const moe_config_t* cfg, int64_t T) {
-  if (check_cfg(cfg, false) != MOE_OK || T < 0) return 0;
+  if (check_cfg(cfg, false) != MOE_OK || T < 0 || T > kMaxTokens) return 0;
   return layout(cfg, T).total;
+}
+
+moe_status_t moe_workspace_region(const moe_config_t* cfg, int64_t T, int32_t region, size_t* offset,
+                                  size_t* bytes) {
+  g_err.clear();
+  TRY(check_cfg(cfg, false));
+  TRY(check_T(T));
+  if (!offset || !bytes) return fail(MOE_ERR_INVALID_ARG, "offset and bytes must not be NULL");
+  if (region < 0 || region >= MOE_WS_COUNT) return fail(MOE_ERR_INVALID_ARG, "region %d out of range", region);
+  const Layout L = layout(cfg, T);
+  const int64_t k = cfg->num_experts_per_tok, H = cfg->hidden_size, F = cfg->moe_intermediate_size;
+  const int64_t Fs = shared_F(cfg), asz = act_size(cfg->act_dtype);
+  const int64_t hsz = fp8(cfg) ? 4 : asz;
+  const bool q = fp8(cfg);
+  size_t o = 0;
+  int64_t n = 0;
+  switch (region) {
+    case MOE_WS_H: o = L.h; n = T * k * F * hsz; break;
+    case MOE_WS_H_CODES: o = L.hq; n = q ? T * k * F : 0; break;
+    case MOE_WS_H_SCALES: o = L.hs; n = q ? T * k * (F / 128) * 4 : 0; break;
+    case MOE_WS_H_SHARED: o = L.hsh; n = T * Fs * hsz; break;
+    case MOE_WS_H_SHARED_CODES: o = L.hqsh; n = q ? T * Fs : 0; break;
+    case MOE_WS_H_SHARED_SCALES: o = L.hssh; n = q ? T * (Fs / 128) * 4 : 0; break;
+    case MOE_WS_Y: o = L.y; n = T * k * H * asz; break;
+    case MOE_WS_Y_SHARED: o = L.ysh; n = T * H * asz; break;
+  }
+  *offset = o;
+  *bytes = static_cast<size_t>(n);
+  return MOE_OK;
 }
 
 moe_status_t moe_profile_arm(int32_t kid, void* start, void* stop) {
@@ -479,10 +514,12 @@ moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* 
     uint8_t* xq = at<uint8_t>(ws, L.xq);
     float* xs = at<float>(ws, L.xs);
     MOE_LAUNCH(MOE_KID_ACT_QUANT, launch_act_quant(static_cast<const uint16_t*>(x), T, H, xq, xs, st));
-    MOE_LAUNCH(MOE_KID_GATHER, launch_gather(xq, sorted_token_ids, TK, H, x_perm, st));
-    MOE_LAUNCH(MOE_KID_GATHER, launch_gather(xs, sorted_token_ids, TK, (H / 128) * 4, x_perm_scales, st));
+    const int32_t* n_rows = expert_offsets + cfg->n_routed_experts;
+    MOE_LAUNCH(MOE_KID_GATHER, launch_gather(xq, sorted_token_ids, TK, n_rows, H, x_perm, st));
+    MOE_LAUNCH(MOE_KID_GATHER, launch_gather(xs, sorted_token_ids, TK, n_rows, (H / 128) * 4, x_perm_scales, st));
   } else {
-    MOE_LAUNCH(MOE_KID_GATHER, launch_gather(x, sorted_token_ids, TK, H * act_size(cfg->act_dtype), x_perm, st));
+    MOE_LAUNCH(MOE_KID_GATHER, launch_gather(x, sorted_token_ids, TK, expert_offsets + cfg->n_routed_experts,
+                                             H * act_size(cfg->act_dtype), x_perm, st));
   }
   return MOE_OK;
 }

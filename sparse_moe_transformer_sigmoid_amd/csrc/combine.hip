@@ -6,7 +6,9 @@
 //   out[t] = resid[t] + y_shared[t] + sum_j w[t][j] * y[inv[t*k + j]].
 // fp32 accumulation in that order, one rounding at the end; one block per
 // token, 16-byte vectors (a wave reads 1 KB of a row per instruction; the
-// routed and shared rows, read once, with the nontemporal hint).
+// routed and shared rows, read once, with the nontemporal hint).  A slot whose
+// inverse index lies outside [0, T*k) -- a pair the grouping did not place,
+// inverse index -1 -- contributes nothing.  Up to 32 slots per token.
 #include "kernels.h"
 
 namespace moe {
@@ -17,8 +19,9 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
   __shared__ int64_t rs[32];
   const int64_t t = blockIdx.x;
   if (threadIdx.x < a.k) {
+    const int64_t r = a.inv[t * a.k + threadIdx.x];
     ws[threadIdx.x] = a.w[t * a.k + threadIdx.x];
-    rs[threadIdx.x] = a.inv[t * a.k + threadIdx.x];
+    rs[threadIdx.x] = r >= 0 && r < static_cast<int64_t>(a.T) * a.k ? r : -1;
   }
   __syncthreads();
   constexpr int VEC = BF16 ? 8 : 4;
@@ -57,10 +60,11 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
         uint4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (j0 + u < a.k) v[u] = load_nt(reinterpret_cast<const uint4*>(y + rs[j0 + u] * a.H) + c);
+          if (j0 + u < a.k && rs[j0 + u] >= 0) v[u] = load_nt(reinterpret_cast<const uint4*>(y + rs[j0 + u] * a.H) + c);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           if (j0 + u >= a.k) break;
+          if (rs[j0 + u] < 0) continue;
           const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
           const float wj = ws[j0 + u];
 #pragma unroll
@@ -88,6 +92,7 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
         acc[0] += s.x; acc[1] += s.y; acc[2] += s.z; acc[3] += s.w;
       }
       for (int j = 0; j < a.k; ++j) {
+        if (rs[j] < 0) continue;
         float4 v = reinterpret_cast<const float4*>(y + rs[j] * a.H)[c];
         const float wj = ws[j];
         acc[0] = fmaf(wj, v.x, acc[0]); acc[1] = fmaf(wj, v.y, acc[1]);

@@ -284,8 +284,11 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     // activation_scheme dynamic), held by the four waves wm of a row half
     // wn, 16 values per lane.  s = amax / 448 (1 for an all-zero group),
     // codes e4m3(h / s) with the division in fp32 -- the same arithmetic as
-    // the activation-quant kernel.  The row maxima meet in LDS (stage 0 is
-    // free once the K loop has drained).
+    // the activation-quant kernel.  The row maxima meet in LDS, in the
+    // weight-scale table: no DMA ever targets it (a stage may still receive a
+    // refill that another wave issued in the last step, which only that
+    // wave's own vmcnt(0) above waits for), and the last step's barrier came
+    // after every wave's reads of the table (lgkmcnt(0)).
     float hv[2][16], rmax[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -297,7 +300,8 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
       }
       rmax[n] = fmaxf(m, __shfl_xor(m, 32, 64));
     }
-    float* gmax = reinterpret_cast<float*>(st0);   // [4 wm][128 rows]
+    static_assert(sizeof(wscale) >= 4 * kBM * sizeof(float), "row maxima fit the scale table");
+    float* gmax = &wscale[0][0][0];   // [4 wm][128 rows]
     if (kh == 0) {
 #pragma unroll
       for (int n = 0; n < 2; ++n) gmax[128 * wm + 64 * wn + 32 * n + r32] = rmax[n];

@@ -55,9 +55,10 @@ struct TileArgs {
 int64_t max_tiles(int64_t T, int k, int E, bool shared, int bm);
 hipError_t launch_build_tiles(const TileArgs& a, hipStream_t st);
 
-// gather rows: dst[p] = src[rows[p]] for p < n, row_bytes per row (multiple of 16)
-hipError_t launch_gather(const void* src, const int32_t* rows, int64_t n, int64_t row_bytes,
-                         void* dst, hipStream_t st);
+// gather rows: dst[p] = src[rows[p]] for p < min(n, *n_rows) (n_rows a device
+// int), row_bytes per row (multiple of 16)
+hipError_t launch_gather(const void* src, const int32_t* rows, int64_t n, const int32_t* n_rows,
+                         int64_t row_bytes, void* dst, hipStream_t st);
 
 // dynamic fp8 quantisation of bf16 / fp32 rows: codes [R][C] e4m3, scales [R][C/128]
 hipError_t launch_act_quant(const uint16_t* src, int64_t R, int C, uint8_t* codes, float* scales,

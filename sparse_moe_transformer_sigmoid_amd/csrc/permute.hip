@@ -1,13 +1,25 @@
 // Grouping of (token, slot) pairs by expert: per-chunk histograms (LDS
 // atomics), a per-expert scan over chunks plus an exclusive scan over experts,
-// and a stable scatter.  Stability comes from 64-bit token masks: for a run
-// of 64 tokens every pair ORs its token bit into its expert's LDS mask (OR is
+// and a stable scatter.  Stability comes from 64-bit masks: for a run of 64
+// tokens every pair ORs its token bit into its expert's LDS mask (OR is
 // order-independent), and its row is the expert's running base plus the
 // number of lower token bits set -- no dependence on atomic arrival order, so
 // the result is the same bit for bit on every run.
+//
+// Ids come from the caller of moe_permute as well as from the router, so any
+// int32 values are handled: a pair whose id lies outside [0, E) is not
+// grouped (not counted, inverse map -1), and a token that names one expert in
+// several slots -- which the token masks cannot tell apart -- sends its run
+// of 64 tokens down a slower path with one mask bit per (token, slot) pair,
+// in flat order t * k + j.  Either way the grouped order is the stable sort of
+// the valid pairs by expert.
 #include "kernels.h"
 
 namespace moe {
+
+__device__ __forceinline__ bool valid_id(int e, int E) {
+  return static_cast<unsigned>(e) < static_cast<unsigned>(E);
+}
 
 __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int T, int k,
                                                   int E, int32_t* __restrict__ chunk_counts) {
@@ -17,7 +29,10 @@ __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ id
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kPermChunk;
   const int64_t n = min(static_cast<int64_t>(kPermChunk), T - t0) * k;
   const int32_t* p = ids + t0 * k;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&cnt[p[i]], 1);
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = p[i];
+    if (valid_id(e, E)) atomicAdd(&cnt[e], 1);
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     chunk_counts[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
@@ -47,7 +62,7 @@ __device__ int block_exclusive_scan(int v, int* total) {
 
 // one block of 1024 threads; thread e owns expert e (E <= 1024)
 __global__ __launch_bounds__(1024) void perm_scan(const int32_t* __restrict__ chunk_counts,
-                                                  int nchunk, int E, int64_t total_rows,
+                                                  int nchunk, int E,
                                                   int32_t* __restrict__ chunk_base,
                                                   int32_t* __restrict__ offsets) {
   const int e = threadIdx.x;
@@ -65,7 +80,67 @@ __global__ __launch_bounds__(1024) void perm_scan(const int32_t* __restrict__ ch
     offsets[e] = off;
     for (int c = 0; c < nchunk; ++c) chunk_base[static_cast<int64_t>(c) * E + e] += off;
   }
-  if (e == 0) offsets[E] = static_cast<int32_t>(total_rows);
+  if (e == 0) offsets[E] = all;   // the grouped (valid) pairs
+}
+
+// Stable scatter of the pairs of tokens [g0, g0 + ntok), ntok <= 64, whose
+// experts' rows start at run[e] (advanced past them on return).  Every thread
+// of the block calls it; `mask` [E] and `flag` are LDS scratch.
+__device__ void scatter_run(const int32_t* __restrict__ ids, int g0, int ntok, int k, int E,
+                            unsigned long long* mask, int32_t* run, int* flag,
+                            int32_t* __restrict__ sorted, int32_t* __restrict__ inv) {
+  const int n = ntok * k, tid = threadIdx.x, nt = blockDim.x;
+  const int64_t base = static_cast<int64_t>(g0) * k;
+  for (int e = tid; e < E; e += nt) mask[e] = 0ull;
+  if (tid == 0) *flag = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += nt) {
+    const int e = ids[base + i];
+    if (!valid_id(e, E)) continue;
+    const unsigned long long bit = 1ull << (i / k);
+    if (atomicOr(&mask[e], bit) & bit) atomicOr(flag, 1);   // expert repeated by a token
+  }
+  __syncthreads();
+  if (*flag == 0) {
+    // token masks: a pair's row is its expert's base + the lower tokens
+    // routed to it
+    for (int i = tid; i < n; i += nt) {
+      const int tl = i / k, e = ids[base + i];
+      int pos = -1;
+      if (valid_id(e, E)) {
+        pos = run[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
+        sorted[pos] = g0 + tl;
+      }
+      inv[base + i] = pos;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += nt) run[e] += __popcll(mask[e]);
+    __syncthreads();
+    return;
+  }
+  // a repeated expert: one bit per pair, 64 flat pairs at a time
+  for (int q0 = 0; q0 < n; q0 += 64) {
+    const int m = min(64, n - q0);
+    for (int e = tid; e < E; e += nt) mask[e] = 0ull;
+    __syncthreads();
+    for (int i = tid; i < m; i += nt) {
+      const int e = ids[base + q0 + i];
+      if (valid_id(e, E)) atomicOr(&mask[e], 1ull << i);
+    }
+    __syncthreads();
+    for (int i = tid; i < m; i += nt) {
+      const int e = ids[base + q0 + i];
+      int pos = -1;
+      if (valid_id(e, E)) {
+        pos = run[e] + __popcll(mask[e] & ((1ull << i) - 1ull));
+        sorted[pos] = g0 + (q0 + i) / k;
+      }
+      inv[base + q0 + i] = pos;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += nt) run[e] += __popcll(mask[e]);
+    __syncthreads();
+  }
 }
 
 __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ ids, int T, int k,
@@ -73,34 +148,16 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ sorted,
                                                     int32_t* __restrict__ inv, int identity_tail) {
   extern __shared__ unsigned long long smem[];
+  __shared__ int flag;
   unsigned long long* mask = smem;                            // [E]
   int32_t* run = reinterpret_cast<int32_t*>(smem + E);        // [E]
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     run[e] = chunk_base[static_cast<int64_t>(blockIdx.x) * E + e];
   const int t_begin = blockIdx.x * kPermChunk;
   const int t_end = min(t_begin + kPermChunk, T);
-  for (int g0 = t_begin; g0 < t_end; g0 += 64) {
-    for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
-    __syncthreads();
-    const int n = min(64, t_end - g0) * k;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const int tl = i / k;
-      const int e = ids[static_cast<int64_t>(g0) * k + i];
-      atomicOr(&mask[e], 1ull << tl);
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const int tl = i / k;
-      const int64_t flat = static_cast<int64_t>(g0) * k + i;
-      const int e = ids[flat];
-      const int pos = run[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
-      sorted[pos] = g0 + tl;
-      inv[flat] = pos;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) run[e] += __popcll(mask[e]);
-    __syncthreads();
-  }
+  // (scatter_run's first barrier orders these run[] writes before their use)
+  for (int g0 = t_begin; g0 < t_end; g0 += 64)
+    scatter_run(ids, g0, min(64, t_end - g0), k, E, mask, run, &flag, sorted, inv);
   if (identity_tail)
     for (int t = t_begin + threadIdx.x; t < t_end; t += blockDim.x)
       sorted[static_cast<int64_t>(T) * k + t] = t;
@@ -113,13 +170,17 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ 
 // (decode) are bound by launch latency, so one launch instead of four.
 __global__ __launch_bounds__(1024) void perm_single(PermArgs a) {
   extern __shared__ unsigned long long smem[];
+  __shared__ int flag;
   unsigned long long* mask = smem;                               // [E]
   int32_t* run = reinterpret_cast<int32_t*>(smem + a.E);         // [E]
   const int E = a.E, T = a.T, k = a.k, tid = threadIdx.x;
   const int n_all = T * k;
   for (int e = tid; e < E; e += blockDim.x) run[e] = 0;
   __syncthreads();
-  for (int i = tid; i < n_all; i += blockDim.x) atomicAdd(&run[a.ids[i]], 1);
+  for (int i = tid; i < n_all; i += blockDim.x) {
+    const int e = a.ids[i];
+    if (valid_id(e, E)) atomicAdd(&run[e], 1);
+  }
   __syncthreads();
   const int cnt = tid < E ? run[tid] : 0;
   int all;
@@ -128,24 +189,10 @@ __global__ __launch_bounds__(1024) void perm_single(PermArgs a) {
     a.offsets[tid] = off;
     run[tid] = off;
   }
-  if (tid == 0) a.offsets[E] = n_all;
-  __syncthreads();
-  for (int g0 = 0; g0 < T; g0 += 64) {
-    for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
-    __syncthreads();
-    const int n = min(64, T - g0) * k;
-    for (int i = tid; i < n; i += blockDim.x) atomicOr(&mask[a.ids[g0 * k + i]], 1ull << (i / k));
-    __syncthreads();
-    for (int i = tid; i < n; i += blockDim.x) {
-      const int tl = i / k, flat = g0 * k + i, e = a.ids[flat];
-      const int pos = run[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
-      a.sorted[pos] = g0 + tl;
-      a.inv[flat] = pos;
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += blockDim.x) run[e] += __popcll(mask[e]);
-    __syncthreads();
-  }
+  if (tid == 0) a.offsets[E] = all;   // the grouped (valid) pairs
+  // (scatter_run's first barrier orders these run[] writes before their use)
+  for (int g0 = 0; g0 < T; g0 += 64)
+    scatter_run(a.ids, g0, min(64, T - g0), k, E, mask, run, &flag, a.sorted, a.inv);
   if (a.identity_tail)
     for (int t = tid; t < T; t += blockDim.x) a.sorted[n_all + t] = t;
   if (a.tiles == nullptr) return;
@@ -184,8 +231,8 @@ hipError_t launch_permute(const PermArgs& a, hipStream_t st, bool* tiles_built) 
                      a.k, a.E, a.chunk_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, st, a.chunk_counts, nchunk, a.E,
-                     static_cast<int64_t>(a.T) * a.k, a.chunk_base, a.offsets);
+  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, st, a.chunk_counts, nchunk, a.E, a.chunk_base,
+                     a.offsets);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(perm_scatter, dim3(nchunk), dim3(256), a.E * (sizeof(unsigned long long) + 4),
@@ -243,22 +290,24 @@ hipError_t launch_build_tiles(const TileArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// row gather (16-byte vectors), one block per 4 rows
+// row gather (16-byte vectors), one block per 4 rows; rows [*n_rows, n) (pairs
+// that were not grouped) are left alone
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gather_rows(const uint4* __restrict__ src,
                                                    const int32_t* __restrict__ rows, int64_t n,
+                                                   const int32_t* __restrict__ n_rows,
                                                    int64_t vec_per_row, uint4* __restrict__ dst) {
   const int64_t p = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (p >= n) return;
+  if (p >= n || p >= *n_rows) return;
   const uint4* s = src + static_cast<int64_t>(rows[p]) * vec_per_row;
   uint4* d = dst + p * vec_per_row;
   for (int64_t i = threadIdx.x & 63; i < vec_per_row; i += 64) d[i] = s[i];
 }
 
-hipError_t launch_gather(const void* src, const int32_t* rows, int64_t n, int64_t row_bytes,
-                         void* dst, hipStream_t st) {
+hipError_t launch_gather(const void* src, const int32_t* rows, int64_t n, const int32_t* n_rows,
+                         int64_t row_bytes, void* dst, hipStream_t st) {
   hipLaunchKernelGGL(gather_rows, dim3((n + 3) / 4), dim3(256), 0, st,
-                     static_cast<const uint4*>(src), rows, n, row_bytes / 16,
+                     static_cast<const uint4*>(src), rows, n, n_rows, row_bytes / 16,
                      static_cast<uint4*>(dst));
   return hipGetLastError();
 }

@@ -170,7 +170,12 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 // ---------------------------------------------------------------------------
 // top-k: one wave per token, 4 tokens per block.  Lane l holds experts
 // l*V .. l*V+V-1.  Each of the k rounds takes the wave-wide maximum of the
-// remaining eligible sel values (ties: lower expert id) by butterfly shuffles.
+// remaining sel values (ties: lower expert id) by butterfly shuffles.
+// Every round picks some expert not taken yet, so a token always gets k
+// distinct ids in [0, E) (k <= E): a NaN sel (NaN or infinite x or router
+// weights) orders as -inf, and experts of groups that were not kept, or with
+// a -inf bias, are -inf as well -- they are taken, lowest id first, only when
+// fewer than k finite eligible scores remain.
 // ---------------------------------------------------------------------------
 template <int V>
 __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ logits, int kparts,
@@ -204,12 +209,18 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
       for (int p = 1; p < kMaxParts; ++p)
         if (p < kparts) z += zp[p][i];
       s[i] = 1.0f / (1.0f + expf(-z));
-      sel[i] = s[i] + bias[e];
+      const float v = s[i] + bias[e];
+      sel[i] = v == v ? v : -INFINITY;
     } else {
       s[i] = 0.f;
       sel[i] = -INFINITY;
     }
   }
+  // experts this lane may still pick (not past E, not taken)
+  uint32_t avail = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+    if (lane * V + i < E) avail |= 1u << i;
   if (n_group > 1) {  // block-uniform branch
     const int gsz = E / n_group;
 #pragma unroll
@@ -223,6 +234,7 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
         if (v > b1) { b2 = b1; b1 = v; } else if (v > b2) { b2 = v; }
       }
       gscore = gsz > 1 ? b1 + b2 : b1;
+      if (!(gscore == gscore)) gscore = -INFINITY;   // +inf + -inf
       gsc_lds[wave][lane] = gscore;
     }
     __syncthreads();
@@ -247,11 +259,14 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
   int my_id = 0;
   float my_s = 0.f;
   for (int r = 0; r < k; ++r) {
+    // the lane's best available expert (ids ascend with i: the first of
+    // equal values wins); a lane with none offers id 0x7fffffff, which any
+    // available expert beats (its value is >= -inf, its id lower)
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < V; ++i)
-      if (sel[i] > bv) { bv = sel[i]; bi = lane * V + i; }
+      if (((avail >> i) & 1u) && (bi == 0x7fffffff || sel[i] > bv)) { bv = sel[i]; bi = lane * V + i; }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float ov = __shfl_xor(bv, o, 64);
@@ -264,11 +279,7 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
     for (int i = 0; i < V; ++i)
       if (i == slot) cand = s[i];
     const float sw = __shfl(cand, owner, 64);
-    if (lane == owner) {
-#pragma unroll
-      for (int i = 0; i < V; ++i)
-        if (i == slot) sel[i] = -INFINITY;
-    }
+    if (lane == owner) avail &= ~(1u << slot);
     if (lane == r) { my_id = bi; my_s = sw; }
   }
   // ascending ids: rank of my_id among the k chosen

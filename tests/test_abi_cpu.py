@@ -191,3 +191,35 @@ def test_block_forward_validates_norm_arguments():
     st = lib.moe_block_forward(ctypes.byref(c), ctypes.byref(w), None, FAKE, ctypes.c_float(1e-6), FAKE, FAKE, 0,
                                None, None, None, None, 0, None)
     assert st == B.MOE_OK  # T = 0: nothing touched
+
+
+def test_workspace_regions_lie_inside_the_workspace():
+    """moe_workspace_region: every region of a K2 bf16 and an fp8 layout lies
+    inside moe_workspace_size, regions do not overlap, and the sizes follow
+    the shapes; bad arguments are rejected."""
+    for name in ("k2_decode_bf16", "k2_fp8"):
+        wl = gen.WORKLOADS[name]
+        c = B.MoeConfig.from_fields(wl.fields())
+        T, k, H, F = 128, 8, 7168, 2048
+        total = B.moe_workspace_size(c, T)
+        spans = []
+        for r in range(B.MOE_WS_COUNT):
+            off, n = B.moe_workspace_region(c, T, r)
+            assert off % 256 == 0 and off + n <= total
+            if n:
+                spans.append((off, off + n))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+        fp8 = name == "k2_fp8"
+        assert B.moe_workspace_region(c, T, B.MOE_WS_H_CODES)[1] == (T * k * F if fp8 else 0)
+        assert B.moe_workspace_region(c, T, B.MOE_WS_H_SCALES)[1] == (T * k * F // 128 * 4 if fp8 else 0)
+        assert B.moe_workspace_region(c, T, B.MOE_WS_Y)[1] == T * k * H * 2
+    lib = B.load()
+    off, n = ctypes.c_size_t(), ctypes.c_size_t()
+    c = k2cfg()
+    assert lib.moe_workspace_region(ctypes.byref(c), 4, B.MOE_WS_COUNT, ctypes.byref(off), ctypes.byref(n)) \
+        == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_region(ctypes.byref(c), 4, 0, None, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_region(ctypes.byref(c), 65537, 0, ctypes.byref(off), ctypes.byref(n)) \
+        == B.MOE_ERR_INVALID_ARG
+    assert B.moe_workspace_size(c, 65537) == 0

@@ -388,6 +388,107 @@ def test_p10_stable_permutation_bruteforce():
     check_permutation()
 
 
+def check_permutation_worked_example():
+    """Hand-derived: E = 3, k = 2, ids [[2, 0], [2, 2], [-1, 1]] (token 1
+    names expert 2 twice, token 2 names no expert in slot 0).  Expert 0 gets
+    pair (0,1); expert 1 pair (2,1); expert 2 pairs (0,0), (1,0), (1,1) in
+    flat order; pair (2,0) is not grouped."""
+    offsets, sorted_ids, inv = oracle.permute(np.array([[2, 0], [2, 2], [-1, 1]]), 3)
+    assert offsets.tolist() == [0, 1, 2, 5]
+    assert sorted_ids.tolist() == [0, 2, 0, 1, 1]
+    assert inv.tolist() == [2, 0, 3, 4, -1, 1]
+
+
+def check_permutation_general(seed=11):
+    """Loop definition on random ids with repeats and out-of-range values:
+    walk experts in order, pairs in flat order; out-of-range pairs get -1."""
+    rng = np.random.default_rng(seed)
+    T, k, E = 50, 4, 7
+    ids = rng.integers(-2, E + 2, (T, k))
+    offsets, sorted_ids, inv = oracle.permute(ids, E)
+    pos, want_sorted, want_inv = 0, [], [-1] * (T * k)
+    for e in range(E):
+        assert offsets[e] == pos
+        for f in range(T * k):
+            if ids[f // k, f % k] == e:
+                want_sorted.append(f // k)
+                want_inv[f] = pos
+                pos += 1
+    assert offsets[E] == pos == int(((ids >= 0) & (ids < E)).sum())
+    assert sorted_ids.tolist() == want_sorted and inv.tolist() == want_inv
+
+
+def test_p10_permutation_with_repeats_and_foreign_ids():
+    check_permutation_worked_example()
+    check_permutation_general()
+
+
+def check_combine():
+    """Hand-derived: y_perm rows [1,2], [3,4], [5,6], [7,8]; shared [[10,0],
+    [0,10]]; weights [[0.5, 2], [1, -1]]; inv [3, 0, -1, 2]:
+    out[0] = [10,0] + 0.5 [7,8] + 2 [1,2] = [15.5, 8];
+    out[1] = [0,10] + (slot 0 not grouped) - [5,6] = [-5, 4]."""
+    y = np.array([[1.0, 2], [3, 4], [5, 6], [7, 8]])
+    out = oracle.combine(y, np.array([[10.0, 0], [0, 10]]), np.array([[0.5, 2], [1, -1]]), np.array([3, 0, -1, 2]))
+    np.testing.assert_array_equal(out, [[15.5, 8], [-5, 4]])
+    out0 = oracle.combine(y, None, np.array([[0.5, 2], [1, -1]]), np.array([3, 0, -1, 2]))
+    np.testing.assert_array_equal(out0, [[5.5, 8], [-5, -6]])
+
+
+def check_combine_is_the_layer_sum(seed=12):
+    """The layer (step 8, each expert applied to its own tokens) equals the
+    combine of the grouped expert outputs: permute, one SwiGLU per segment,
+    combine (every slot grouped)."""
+    rng = np.random.default_rng(seed)
+    T, H, F, E, k = 12, 8, 6, 5, 2
+    x, rw, b = rng.standard_normal((T, H)), rng.standard_normal((E, H)), rng.standard_normal(E) * 0.01
+    ws = [tuple(rng.standard_normal(s) * 0.3 for s in ((F, H), (F, H), (H, F))) for _ in range(E + 1)]
+    ref, r = oracle.layer_forward(x, rw, b, lambda e: ws[e], ws[E], num_experts_per_tok=k)
+    offsets, sorted_ids, inv = oracle.permute(r.ids, E)
+    y = np.zeros((T * k, H))
+    for e in range(E):
+        a, c = offsets[e], offsets[e + 1]
+        if c > a:
+            y[a:c] = om.swiglu_expert(x[sorted_ids[a:c]], *ws[e])
+    out = oracle.combine(y, om.swiglu_expert(x, *ws[E]), r.weights, inv)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_combine_worked_example_and_layer_identity():
+    check_combine()
+    check_combine_is_the_layer_sum()
+
+
+def check_gaps(seed=13):
+    """selection_gap and group_gap by brute force on tiny inputs: the chosen
+    set's smallest sel minus the largest eligible unchosen one; the kept
+    groups' smallest score (top-2 sums taken by a loop) minus the largest
+    dropped one, the kept set being the best of all C(4, 2) subsets."""
+    x, w, b = tiny_router(seed, T=20, E=16, bias_std=0.3)
+    r = oracle.route(x, w, b, num_experts_per_tok=4)
+    gap = oracle.selection_gap(r, 4)
+    for t in range(20):
+        chosen = np.zeros(16, bool)
+        chosen[r.ids[t]] = True
+        assert math.isclose(gap[t], r.sel[t][chosen].min() - r.sel[t][~chosen].max(), rel_tol=0, abs_tol=1e-15)
+    rg = oracle.route(x, w, b, num_experts_per_tok=4, n_group=4, topk_group=2)
+    ggap = oracle.group_gap(rg, 4, 2)
+    for t in range(20):
+        sc = []
+        for g in range(4):
+            v = sorted(rg.sel[t, 4 * g:4 * g + 4].tolist(), reverse=True)
+            sc.append(v[0] + v[1])
+        kept = max(itertools.combinations(range(4), 2), key=lambda s: sum(sc[i] for i in s))
+        dropped = [sc[i] for i in range(4) if i not in kept]
+        assert math.isclose(ggap[t], min(sc[i] for i in kept) - max(dropped), rel_tol=0, abs_tol=1e-15)
+    assert np.all(oracle.group_gap(r, 1, 1) == np.inf)
+    assert np.all(oracle.selection_gap(r, 16) == np.inf)
+
+
+def test_selection_and_group_gaps_bruteforce():
+    check_gaps()
+
+
 # -------------------------------------------------------------------- P11 --
 def test_p11_active_expert_count_matches_expectation():
     # decode bytes scale with the number of distinct experts touched,
@@ -511,8 +612,9 @@ def test_block_is_residual_plus_layer_on_rounded_norm():
 # ------------------------------------------------------ planted mistakes ---
 PINS = [check_param_counts, check_routing_worked_example, check_swiglu_worked_example,
         check_bruteforce_topk, check_bruteforce_grouped, check_identical_experts,
-        check_single_expert, check_e4m3, check_permutation, check_round_bf16, check_rms_norm,
-        check_block]
+        check_single_expert, check_e4m3, check_permutation, check_permutation_worked_example,
+        check_permutation_general, check_combine, check_combine_is_the_layer_sum, check_gaps,
+        check_round_bf16, check_rms_norm, check_block]
 
 
 def _any_pin_fails():
@@ -538,6 +640,14 @@ MUTANTS = {
         lambda sel, ng: np.sort(sel.reshape(sel.shape[0], ng, -1), axis=2)[:, :, -1])),
     "e4m3_truncate": ("e4m3_round", lambda orig: (lambda v: _trunc_e4m3(v))),
     "permute_unstable": ("permute", lambda orig: (lambda ids, E: _unstable_permute(orig, ids, E))),
+    "permute_clips_foreign_ids": ("permute", lambda orig: (lambda ids, E: orig(np.clip(ids, 0, E - 1), E))),
+    "combine_wraps_minus_one": ("combine", lambda orig: (
+        lambda y, ysh, w, inv: orig(y, ysh, w, np.where(np.asarray(inv) < 0, np.asarray(inv) + len(y), inv)))),
+    "combine_drops_shared": ("combine", lambda orig: (lambda y, ysh, w, inv: orig(y, None, w, inv))),
+    "selection_gap_next_pair": ("selection_gap", lambda orig: (
+        lambda r, k: orig(r, k + 1) if k + 1 < r.sel.shape[1] else orig(r, k))),
+    "group_gap_next_pair": ("group_gap", lambda orig: (
+        lambda r, ng, tg: orig(r, ng, tg + 1) if 1 < tg + 1 < ng else orig(r, ng, tg))),
     "expert_params_two_linears": ("expert_params", lambda orig: (lambda h, f: 2 * h * f)),
     "bf16_via_fp32": ("round_bf16", lambda orig: (
         lambda v: torch.from_numpy(np.asarray(v, np.float64).astype(np.float32)).to(torch.bfloat16).double().numpy())),
