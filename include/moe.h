@@ -176,6 +176,23 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
                                void* out, int32_t* topk_ids_out, float* topk_weights_out,
                                void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, bit for bit, with the
+ * workspace taken from a fixed array of MOE_STATIC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on (from the first call on that device
+ * until the process ends).  Calls nothing that allocates.  Rejects, with
+ * MOE_ERR_WORKSPACE and launching nothing, a token count whose workspace
+ * (moe_workspace_size) exceeds MOE_STATIC_SCRATCH_BYTES (Kimi-K2 bf16:
+ * about 330 tokens).  The array is shared by every call on one GPU and keeps
+ * the last call's contents: calls that overlap on one GPU (concurrent
+ * streams or threads) race; order them on one stream.  The device is the
+ * current HIP device of the calling thread. */
+#define MOE_STATIC_SCRATCH_BYTES (64ull << 20)
+moe_status_t moe_layer_forward_static(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                                      const void* router_w, const float* router_bias, int64_t num_tokens,
+                                      void* out, int32_t* topk_ids_out, float* topk_weights_out, void* stream);
+
 /* The MoE sub-block of a decoder layer: the pre-MoE RMSNorm, the layer, and
  * the residual add ("Kimi K2 Base" architecture table: RMSNorm; raw config
  * fields: rms_norm_eps 1e-06):

@@ -99,6 +99,7 @@ def load() -> ctypes.CDLL:
         "moe_expert_ffn": (st, [CP, WP, _P, _P, _P, _P, i64, _P, _P, _P, sz, _P]),
         "moe_combine": (st, [CP, _P, _P, _P, _P, i64, _P, _P]),
         "moe_layer_forward": (st, [CP, WP, _P, _P, _P, i64, _P, _P, _P, _P, sz, _P]),
+        "moe_layer_forward_static": (st, [CP, WP, _P, _P, _P, i64, _P, _P, _P, _P]),
         "moe_block_forward": (st, [CP, WP, _P, _P, ctypes.c_float, _P, _P, i64, _P, _P, _P, _P, sz, _P]),
         "moe_status_string": (ctypes.c_char_p, [st]),
         "moe_last_error": (ctypes.c_char_p, []),
@@ -180,6 +181,19 @@ def moe_layer_forward(cfg, weights: MoeWeights, x, router_w, router_bias, out, w
                                     _ptr(router_bias), x.shape[0], _ptr(out), _ptr(topk_ids),
                                     _ptr(topk_weights), _ptr(ws), _nbytes(ws), _stream(stream)),
            "moe_layer_forward")
+
+
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_layer_forward_static(cfg, weights: MoeWeights, x, router_w, router_bias, out, topk_ids=None,
+                             topk_weights=None, stream=None):
+    """moe_layer_forward on the library's fixed per-GPU scratch (no workspace
+    argument, nothing allocated)."""
+    _check(load().moe_layer_forward_static(ctypes.byref(cfg), ctypes.byref(weights), _ptr(x), _ptr(router_w),
+                                           _ptr(router_bias), x.shape[0], _ptr(out), _ptr(topk_ids),
+                                           _ptr(topk_weights), _stream(stream)),
+           "moe_layer_forward_static")
 
 
 def moe_block_forward(cfg, weights: MoeWeights, x, norm_weight, rms_norm_eps, router_w, router_bias, out, ws,

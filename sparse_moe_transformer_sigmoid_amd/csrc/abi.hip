@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -350,12 +351,10 @@ FfnArgs ffn_args(const moe_config_t* c, int64_t T, void* ws) {
   return f;
 }
 
-moe_status_t check_layer_args(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
-                              const void* router_w, const float* router_bias, int64_t T, void* out,
-                              int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes) {
-  TRY(check_cfg(cfg));
-  TRY(check_T(T));
-  if (T == 0) return MOE_OK;
+// the layer's tensor arguments (after check_cfg, for T > 0)
+moe_status_t check_layer_ptrs(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                              const void* router_w, const float* router_bias, void* out,
+                              int32_t* topk_ids_out, float* topk_weights_out) {
   TRY(check_weights(cfg, w));
   NEED(x);
   NEED(router_w);
@@ -363,6 +362,16 @@ moe_status_t check_layer_args(const moe_config_t* cfg, const moe_weights_t* w, c
   NEED(out);
   if (topk_ids_out && !aligned(topk_ids_out)) return fail(MOE_ERR_INVALID_ARG, "topk_ids_out is not 16-byte aligned");
   if (topk_weights_out && !aligned(topk_weights_out)) return fail(MOE_ERR_INVALID_ARG, "topk_weights_out is not 16-byte aligned");
+  return MOE_OK;
+}
+
+moe_status_t check_layer_args(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                              const void* router_w, const float* router_bias, int64_t T, void* out,
+                              int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes) {
+  TRY(check_cfg(cfg));
+  TRY(check_T(T));
+  if (T == 0) return MOE_OK;
+  TRY(check_layer_ptrs(cfg, w, x, router_w, router_bias, out, topk_ids_out, topk_weights_out));
   return check_ws(cfg, T, ws, ws_bytes);
 }
 
@@ -404,6 +413,39 @@ moe_status_t run_layer(const moe_config_t* cfg, const moe_weights_t* w, const vo
   CombineArgs a{f.y, cfg->n_shared_experts > 0 ? f.y_sh : nullptr, wts, inv, static_cast<int>(T),
                 cfg->num_experts_per_tok, cfg->hidden_size, out, resid};
   MOE_LAUNCH(MOE_KID_COMBINE, launch_combine(a, cfg->act_dtype == MOE_BF16, st));
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The fixed scratch of moe_layer_forward_static: one array per GPU (each
+// device that loads the library holds its own copy until the process ends),
+// standing in for the caller's workspace.  In host code `scratch` is a
+// host-side stand-in, never a device address: its device address is taken
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that pointer is passed on.  Nothing in the workspace needs to start
+// at zero (every piece is written before it is read), so it is not cleared.
+constexpr size_t kStaticScratch = MOE_STATIC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kStaticScratch];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// device address of the current device's scratch array (looked up once)
+moe_status_t static_scratch(void** ptr) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t s = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (s != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(s));
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
   return MOE_OK;
 }
 
@@ -589,6 +631,26 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   g_err.clear();
   TRY(check_layer_args(cfg, w, x, router_w, router_bias, T, out, topk_ids_out, topk_weights_out, ws, ws_bytes));
   if (T == 0) return MOE_OK;
+  (void)hipGetLastError();
+  return run_layer(cfg, w, x, router_w, router_bias, T, out, topk_ids_out, topk_weights_out, ws,
+                   static_cast<hipStream_t>(stream), nullptr, false);
+}
+
+moe_status_t moe_layer_forward_static(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                                      const void* router_w, const float* router_bias, int64_t T, void* out,
+                                      int32_t* topk_ids_out, float* topk_weights_out, void* stream) {
+  g_err.clear();
+  TRY(check_cfg(cfg));
+  TRY(check_T(T));
+  if (T == 0) return MOE_OK;
+  const size_t need = layout(cfg, T).total;
+  if (need > kStaticScratch)
+    return fail(MOE_ERR_WORKSPACE, "%lld tokens need %zu bytes of workspace, more than the %zu of the fixed scratch",
+                (long long)T, need, kStaticScratch);
+  TRY(check_layer_ptrs(cfg, w, x, router_w, router_bias, out, topk_ids_out, topk_weights_out));
+  // (every argument checked before the first HIP call)
+  void* ws = nullptr;
+  TRY(static_scratch(&ws));
   (void)hipGetLastError();
   return run_layer(cfg, w, x, router_w, router_bias, T, out, topk_ids_out, topk_weights_out, ws,
                    static_cast<hipStream_t>(stream), nullptr, false);

@@ -223,3 +223,29 @@ def test_workspace_regions_lie_inside_the_workspace():
     assert lib.moe_workspace_region(ctypes.byref(c), 65537, 0, ctypes.byref(off), ctypes.byref(n)) \
         == B.MOE_ERR_INVALID_ARG
     assert B.moe_workspace_size(c, 65537) == 0
+
+
+def test_static_entry_point_rejects_before_any_gpu_call():
+    """moe_layer_forward_static: a token count whose workspace exceeds the
+    fixed scratch, and bad pointers, are rejected on the host (no GPU here,
+    so a HIP call would fail differently); T = 0 is a no-op."""
+    c = k2cfg()
+    lib = B.load()
+    w = B.MoeWeights()
+    for n in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
+        setattr(w, n, FAKE)
+    limit = B.MOE_STATIC_SCRATCH_BYTES
+    m = re.search(r"#define MOE_STATIC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == limit
+    T_max = max(t for t in range(1, 2048) if B.moe_workspace_size(c, t) <= limit)
+    assert 256 <= T_max < 2048
+    st = lib.moe_layer_forward_static(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, FAKE, T_max + 1, FAKE, None,
+                                      None, None)
+    assert st == B.MOE_ERR_WORKSPACE and "fixed scratch" in B.moe_last_error()
+    st = lib.moe_layer_forward_static(ctypes.byref(c), ctypes.byref(w), None, FAKE, FAKE, 4, FAKE, None, None, None)
+    assert st == B.MOE_ERR_INVALID_ARG and "x is NULL" in B.moe_last_error()
+    st = lib.moe_layer_forward_static(ctypes.byref(c), ctypes.byref(B.MoeWeights()), FAKE, FAKE, FAKE, 4, FAKE,
+                                      None, None, None)
+    assert st == B.MOE_ERR_INVALID_ARG and "w_gate" in B.moe_last_error()
+    assert lib.moe_layer_forward_static(ctypes.byref(c), ctypes.byref(w), None, None, None, 0, None, None, None,
+                                        None) == B.MOE_OK
