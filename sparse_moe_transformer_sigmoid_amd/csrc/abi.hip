@@ -237,10 +237,16 @@ RouterArgs router_args(const moe_config_t* c, const void* x, const void* rw, con
   return a;
 }
 
+// `quant_x`: (fp8 weights) the top-k launch also writes x's e4m3 codes and
+// scales into the workspace
 moe_status_t run_route(const moe_config_t* c, const void* x, const void* rw, const float* b,
-                       int64_t T, int32_t* ids, float* w, void* ws, hipStream_t st) {
+                       int64_t T, int32_t* ids, float* w, void* ws, hipStream_t st, bool quant_x = false) {
   const Layout L = layout(c, T);
   RouterArgs a = router_args(c, x, rw, b, T, at<float>(ws, L.logits), ids, w);
+  if (quant_x) {
+    a.xq_codes = at<uint8_t>(ws, L.xq);
+    a.xq_scales = at<float>(ws, L.xs);
+  }
   MOE_LAUNCH(MOE_KID_ROUTER_LOGITS, launch_router(a, st));
   MOE_LAUNCH(MOE_KID_ROUTER_TOPK, launch_topk(a, st));
   return MOE_OK;
@@ -385,7 +391,8 @@ moe_status_t run_layer(const moe_config_t* cfg, const moe_weights_t* w, const vo
   const Layout L = layout(cfg, T);
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
   float* wts = topk_weights_out ? topk_weights_out : at<float>(ws, L.w);
-  TRY(run_route(cfg, x, router_w, router_bias, T, ids, wts, ws, st));
+  // fp8 weights: the top-k launch quantises x as well (unless the norm pass did)
+  TRY(run_route(cfg, x, router_w, router_bias, T, ids, wts, ws, st, fp8(cfg) && !x_quantised));
   int32_t* offsets = at<int32_t>(ws, L.offsets);
   int32_t* rows = at<int32_t>(ws, L.rows);
   int32_t* inv = at<int32_t>(ws, L.inv);
@@ -402,8 +409,6 @@ moe_status_t run_layer(const moe_config_t* cfg, const moe_weights_t* w, const vo
   if (fp8(cfg)) {
     uint8_t* xq = at<uint8_t>(ws, L.xq);
     float* xs = at<float>(ws, L.xs);
-    if (!x_quantised)
-      MOE_LAUNCH(MOE_KID_ACT_QUANT, launch_act_quant(static_cast<const uint16_t*>(x), T, cfg->hidden_size, xq, xs, st));
     f.xr = xq;
     f.xr_scales = xs;
     f.xs = xq;

@@ -88,6 +88,92 @@ __device__ __forceinline__ uint16_t quant_pair(float v0, float v1, float& s) {
   return static_cast<uint16_t>(f32_to_e4m3(v0 / s)) | (static_cast<uint16_t>(f32_to_e4m3(v1 / s)) << 8);
 }
 
+// ---- dynamic fp8 activation quantisation ------------------------------------
+// ("Kimi K2 . Down projection", config.json quantization_config: fmt e4m3,
+// activation_scheme dynamic.)  Per row and 128-channel group: s = amax / 448
+// (1 for an all-zero group), codes e4m3(v / s) with the division in fp32.
+// Rows come in up to two sets (groups [0, n0) of the first, then those of the
+// second); 16 lanes hold one group (8 values each), a wave GPW groups (4 per
+// load), every load issued before the arithmetic.
+template <typename In>
+struct QuantSeg {
+  const In* src;
+  int64_t R;
+  int C;
+  uint8_t* codes;
+  float* scales;
+};
+
+// 8 consecutive values of a row (16 bytes of bf16, 32 of fp32)
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu));
+    v[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// the groups of block `blk` (4 waves of GPW groups) of a 256-thread launch
+template <typename In, int GPW>
+__device__ __forceinline__ void quant_groups(const QuantSeg<In>& s0, const QuantSeg<In>& s1, int64_t blk) {
+  const int lane = threadIdx.x & 63, sub = lane & 15;
+  const int64_t n0 = s0.R * (s0.C / 128);
+  const int64_t total = n0 + s1.R * (s1.C / 128);
+  const int64_t g0 = (blk * 4 + (threadIdx.x >> 6)) * GPW + (lane >> 4);
+  // group gi: its set, its index inside the set and its first value
+  auto locate = [&](int64_t gi, const QuantSeg<In>*& sg, int64_t& off, int64_t& gs) {
+    sg = gi < n0 ? &s0 : &s1;
+    gs = gi < n0 ? gi : gi - n0;
+    const int groups = sg->C / 128;
+    const int64_t row = gs / groups;
+    off = row * sg->C + (gs - row * groups) * 128 + 8 * sub;
+  };
+  float v[GPW / 4][8];
+#pragma unroll
+  for (int i = 0; i < GPW / 4; ++i) {
+    const int64_t gi = g0 + 4 * i;
+    if (gi < total) {
+      const QuantSeg<In>* sg;
+      int64_t off, gs;
+      locate(gi, sg, off, gs);
+      load8(sg->src + off, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < GPW / 4; ++i) {
+    const int64_t gi = g0 + 4 * i;
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[i][e]));
+    // the group's 16 lanes (xor offsets below 16 stay inside them)
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    if (gi >= total) continue;   // (after the shuffles, which every lane joins)
+    const float sc = m > 0.f ? m / 448.0f : 1.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo |= static_cast<uint32_t>(f32_to_e4m3(v[i][e] / sc)) << (8 * e);
+      hi |= static_cast<uint32_t>(f32_to_e4m3(v[i][4 + e] / sc)) << (8 * e);
+    }
+    const QuantSeg<In>* sg;
+    int64_t off, gs;
+    locate(gi, sg, off, gs);
+    *reinterpret_cast<uint2*>(sg->codes + off) = make_uint2(lo, hi);
+    if (sub == 0) sg->scales[gs] = sc;
+  }
+}
+
 // ---- grouped-GEMM work list ----------------------------------------------
 // One entry per (group, tile of up to BM grouped rows).  Groups 0..E-1 are the
 // routed experts (rows [offsets[e], offsets[e+1]) of the grouped order), group

@@ -19,8 +19,9 @@
 // compute instead of stalling every step.  As in the bf16 stream, weights
 // are loaded in whole 128-byte lines with the nontemporal hint and pass
 // through a per-wave LDS scratch into the MFMA layout.
-// The SwiGLU output is written in fp32; the activation-quant kernel turns it
-// into e4m3 codes + per-128 scales for the down projection.
+// The SwiGLU output is written in fp32; one activation-quant launch turns the
+// routed and shared rows into e4m3 codes + per-128 scales for the down
+// projection.
 #include "kernels.h"
 
 namespace moe {
@@ -304,12 +305,12 @@ hipError_t launch_gate_up_fp8(const FfnArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // SwiGLU output -> e4m3 codes + per-128 scales for the down projection
-  e = launch_act_quant_f32(static_cast<const float*>(a.h), static_cast<int64_t>(a.T) * a.k, a.F,
-                           static_cast<uint8_t*>(a.hq), a.h_scales, st);
-  if (e != hipSuccess || a.Fs == 0) return e;
-  return launch_act_quant_f32(static_cast<const float*>(a.h_sh), a.T, a.Fs,
-                              static_cast<uint8_t*>(a.hq_sh), a.h_sh_scales, st);
+  // SwiGLU output (routed and shared rows, one launch) -> e4m3 codes +
+  // per-128 scales for the down projection
+  return launch_act_quant_f32(static_cast<const float*>(a.h), static_cast<int64_t>(a.T) * a.k, a.F,
+                              static_cast<uint8_t*>(a.hq), a.h_scales, static_cast<const float*>(a.h_sh),
+                              a.Fs > 0 ? a.T : 0, a.Fs > 0 ? a.Fs : 128, static_cast<uint8_t*>(a.hq_sh),
+                              a.h_sh_scales, st);
 }
 
 hipError_t launch_down_fp8(const FfnArgs& a, hipStream_t st) {

@@ -16,6 +16,10 @@ struct RouterArgs {
   float* logits;  // [T][E] scratch
   int32_t* ids;   // [T][k]
   float* w;       // [T][k]
+  // optional (fp8 expert weights): the top-k launch also quantises x (bf16)
+  // per token and 128 channels into codes [T][H] and scales [T][H/128]
+  uint8_t* xq_codes = nullptr;
+  float* xq_scales = nullptr;
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t st);
 // K parts of the router logits (partial sums [kparts][T][E] in the logits scratch)
@@ -63,7 +67,9 @@ hipError_t launch_gather(const void* src, const int32_t* rows, int64_t n, const 
 // dynamic fp8 quantisation of bf16 / fp32 rows: codes [R][C] e4m3, scales [R][C/128]
 hipError_t launch_act_quant(const uint16_t* src, int64_t R, int C, uint8_t* codes, float* scales,
                             hipStream_t st);
+// the same for fp32 rows, in one launch over two row sets (R2 may be 0)
 hipError_t launch_act_quant_f32(const float* src, int64_t R, int C, uint8_t* codes, float* scales,
+                                const float* src2, int64_t R2, int C2, uint8_t* codes2, float* scales2,
                                 hipStream_t st);
 
 // grouped expert FFN

@@ -314,99 +314,38 @@ hipError_t launch_gather(const void* src, const int32_t* rows, int64_t n, const 
 
 // ---------------------------------------------------------------------------
 // dynamic activation quantisation ("Kimi K2 . Down projection", config.json
-// quantization_config: fmt e4m3, activation_scheme dynamic): per row and 128
-// channels s = amax / 448 (1 when the group is all zero), code = e4m3(v / s).
-// One wave per group of 128: two values per lane.
+// quantization_config: fmt e4m3, activation_scheme dynamic), the body in
+// common.h (quant_groups), one block per 16 or 32 groups
 // ---------------------------------------------------------------------------
-// 8 consecutive values of a row (16 bytes of bf16, 32 of fp32)
-__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
-  const uint4 q = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu));
-    v[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
-  }
-}
-__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+template <typename In, int GPW>
+__global__ __launch_bounds__(256) void act_quant_rows(QuantSeg<In> s0, QuantSeg<In> s1) {
+  quant_groups<In, GPW>(s0, s1, blockIdx.x);
 }
 
-// Dynamic activation quantisation, per row and 128-channel group: s = amax /
-// 448 (1 for an all-zero group), codes e4m3(v / s) with the division in fp32.
-// 16 lanes hold one group (8 values each), so a wave covers 4 groups per
-// load and GPW groups in all, every load issued before the arithmetic.
-template <typename In, int GPW>
-__global__ __launch_bounds__(256) void act_quant_rows(const In* __restrict__ src, int64_t R, int C,
-                                                      uint8_t* __restrict__ codes,
-                                                      float* __restrict__ scales) {
-  const int lane = threadIdx.x & 63, sub = lane & 15;
-  const int groups = C / 128;
-  const int64_t total = R * groups;
-  const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * GPW + (lane >> 4);
-  float v[GPW / 4][8];
-#pragma unroll
-  for (int i = 0; i < GPW / 4; ++i) {
-    const int64_t gi = g0 + 4 * i;
-    if (gi < total) {
-      const int64_t row = gi / groups;
-      load8(src + row * C + (gi - row * groups) * 128 + 8 * sub, v[i]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < GPW / 4; ++i) {
-    const int64_t gi = g0 + 4 * i;
-    float m = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[i][e]));
-    // the group's 16 lanes (xor offsets below 16 stay inside them)
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-    if (gi >= total) continue;   // (after the shuffles, which every lane joins)
-    const float sc = m > 0.f ? m / 448.0f : 1.0f;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lo |= static_cast<uint32_t>(f32_to_e4m3(v[i][e] / sc)) << (8 * e);
-      hi |= static_cast<uint32_t>(f32_to_e4m3(v[i][4 + e] / sc)) << (8 * e);
-    }
-    const int64_t row = gi / groups;
-    const int64_t off = row * C + (gi - row * groups) * 128 + 8 * sub;
-    *reinterpret_cast<uint2*>(codes + off) = make_uint2(lo, hi);
-    if (sub == 0) scales[gi] = sc;
-  }
+template <typename In>
+static hipError_t launch_quant(QuantSeg<In> s0, QuantSeg<In> s1, hipStream_t st) {
+  const int64_t groups = s0.R * (s0.C / 128) + s1.R * (s1.C / 128);
+  if (groups == 0) return hipSuccess;
+  // 8 groups per wave on large inputs (two loads in flight per lane), 4 on
+  // small ones, where the grid would be too small to fill the chip
+  if (groups >= (1 << 16))
+    hipLaunchKernelGGL((act_quant_rows<In, 8>), dim3((groups + 31) / 32), dim3(256), 0, st, s0, s1);
+  else
+    hipLaunchKernelGGL((act_quant_rows<In, 4>), dim3((groups + 15) / 16), dim3(256), 0, st, s0, s1);
+  return hipGetLastError();
 }
 
 hipError_t launch_act_quant(const uint16_t* src, int64_t R, int C, uint8_t* codes, float* scales,
                             hipStream_t st) {
-  const int64_t groups = R * (C / 128);
-  // 8 groups per wave on large inputs (two loads in flight per lane), 4 on
-  // small ones, where the grid would be too small to fill the chip
-  if (groups >= (1 << 16))
-    hipLaunchKernelGGL((act_quant_rows<uint16_t, 8>), dim3((groups + 31) / 32), dim3(256), 0, st, src, R, C,
-                       codes, scales);
-  else
-    hipLaunchKernelGGL((act_quant_rows<uint16_t, 4>), dim3((groups + 15) / 16), dim3(256), 0, st, src, R, C,
-                       codes, scales);
-  return hipGetLastError();
+  return launch_quant(QuantSeg<uint16_t>{src, R, C, codes, scales}, QuantSeg<uint16_t>{src, 0, C, codes, scales},
+                      st);
 }
 
 hipError_t launch_act_quant_f32(const float* src, int64_t R, int C, uint8_t* codes, float* scales,
+                                const float* src2, int64_t R2, int C2, uint8_t* codes2, float* scales2,
                                 hipStream_t st) {
-  const int64_t groups = R * (C / 128);
-  if (groups == 0) return hipSuccess;
-  if (groups >= (1 << 16))
-    hipLaunchKernelGGL((act_quant_rows<float, 8>), dim3((groups + 31) / 32), dim3(256), 0, st, src, R, C,
-                       codes, scales);
-  else
-    hipLaunchKernelGGL((act_quant_rows<float, 4>), dim3((groups + 15) / 16), dim3(256), 0, st, src, R, C,
-                       codes, scales);
-  return hipGetLastError();
+  return launch_quant(QuantSeg<float>{src, R, C, codes, scales}, QuantSeg<float>{src2, R2, C2, codes2, scales2},
+                      st);
 }
 
 }  // namespace moe

@@ -169,20 +169,36 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 
 // ---------------------------------------------------------------------------
 // top-k: one wave per token, 4 tokens per block.  Lane l holds experts
-// l*V .. l*V+V-1.  Each of the k rounds takes the wave-wide maximum of the
-// remaining sel values (ties: lower expert id) by butterfly shuffles.
-// Every round picks some expert not taken yet, so a token always gets k
-// distinct ids in [0, E) (k <= E): a NaN sel (NaN or infinite x or router
-// weights) orders as -inf, and experts of groups that were not kept, or with
-// a -inf bias, are -inf as well -- they are taken, lowest id first, only when
-// fewer than k finite eligible scores remain.
+// l*V .. l*V+V-1.  The selection scores become order-preserving 32-bit keys
+// (NaN as -inf, -0 as +0; experts past E key 0, below every score), and the
+// k-th largest key is found bit by bit, 32 steps of "how many keys are >=
+// this", each a compare and a ballot popcount per slot -- scalar work, no
+// cross-lane shuffle chain.  The chosen experts are the keys above it plus
+// the lowest ids among the keys equal to it (ties: lower expert id), and a
+// prefix popcount puts each chosen id at its ascending position.  So a token
+// always gets k distinct ids in [0, E) (k <= E): experts of groups that were
+// not kept, or with a -inf bias, score -inf and are taken, lowest id first,
+// only when fewer than k finite eligible scores remain.
+// With fp8 expert weights the same launch quantises x: blocks from
+// `topk_blocks` on are activation-quant blocks (quant_groups).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);   // (-0 + 0 = +0)
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 template <int V>
 __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ logits, int kparts,
                                                    const float* __restrict__ bias, int T, int E,
                                                    int k, int n_group, int topk_group, int norm,
                                                    float scale, int32_t* __restrict__ ids_out,
-                                                   float* __restrict__ w_out) {
+                                                   float* __restrict__ w_out, int topk_blocks,
+                                                   QuantSeg<uint16_t> xq) {
+  if (static_cast<int>(blockIdx.x) >= topk_blocks) {   // block-uniform: x's fp8 codes
+    quant_groups<uint16_t, 4>(xq, QuantSeg<uint16_t>{xq.src, 0, xq.C, xq.codes, xq.scales},
+                              blockIdx.x - topk_blocks);
+    return;
+  }
   __shared__ float sel_lds[4][64 * V];
   __shared__ float gsc_lds[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -190,15 +206,16 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
   const bool valid = t < T;
   const int tt = valid ? t : T - 1;
   float s[V], sel[V];
-  // partial logits of the K parts (at most kMaxParts), all loaded before
-  // they are added in part order
+  // partial logits of the K parts (at most kMaxParts), all loaded at once
+  // (every load unconditional: a part past kparts re-reads part 0 and is not
+  // added), then added in part order
   float zp[kMaxParts][V];
 #pragma unroll
   for (int p = 0; p < kMaxParts; ++p)
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      const int e = lane * V + i;
-      zp[p][i] = p < kparts && e < E ? logits[(static_cast<int64_t>(p) * T + tt) * E + e] : 0.f;
+      const int e = min(lane * V + i, E - 1);
+      zp[p][i] = logits[(static_cast<int64_t>(p < kparts ? p : 0) * T + tt) * E + e];
     }
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -216,11 +233,6 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
       sel[i] = -INFINITY;
     }
   }
-  // experts this lane may still pick (not past E, not taken)
-  uint32_t avail = 0;
-#pragma unroll
-  for (int i = 0; i < V; ++i)
-    if (lane * V + i < E) avail |= 1u << i;
   if (n_group > 1) {  // block-uniform branch
     const int gsz = E / n_group;
 #pragma unroll
@@ -256,40 +268,50 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ log
       if (e < E && gsc_lds[wave][e / gsz] == 0.f) sel[i] = -INFINITY;
     }
   }
-  int my_id = 0;
-  float my_s = 0.f;
-  for (int r = 0; r < k; ++r) {
-    // the lane's best available expert (ids ascend with i: the first of
-    // equal values wins); a lane with none offers id 0x7fffffff, which any
-    // available expert beats (its value is >= -inf, its id lower)
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+  uint32_t key[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i)
-      if (((avail >> i) & 1u) && (bi == 0x7fffffff || sel[i] > bv)) { bv = sel[i]; bi = lane * V + i; }
+  for (int i = 0; i < V; ++i) key[i] = lane * V + i < E ? order_key(sel[i]) : 0u;
+  auto count = [&](auto pred) {   // wave-wide number of keys satisfying pred
+    int c = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    const int owner = bi / V, slot = bi - owner * V;
-    float cand = 0.f;
-#pragma unroll
-    for (int i = 0; i < V; ++i)
-      if (i == slot) cand = s[i];
-    const float sw = __shfl(cand, owner, 64);
-    if (lane == owner) avail &= ~(1u << slot);
-    if (lane == r) { my_id = bi; my_s = sw; }
+    for (int i = 0; i < V; ++i) c += __popcll(__ballot(pred(key[i])));
+    return c;
+  };
+  // the k-th largest key: the largest thr with at least k keys >= thr
+  uint32_t thr = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = thr | (1u << b);
+    if (count([c](uint32_t x) { return x >= c; }) >= k) thr = c;
   }
-  // ascending ids: rank of my_id among the k chosen
-  int rank = 0;
-  for (int j = 0; j < k; ++j) rank += __shfl(my_id, j, 64) < my_id;
-  const float sum = wave_sum(lane < k ? my_s : 0.f);
-  const float w = norm ? (my_s / sum) * scale : my_s * scale;
-  if (valid && lane < k) {
-    ids_out[static_cast<int64_t>(t) * k + rank] = my_id;
-    w_out[static_cast<int64_t>(t) * k + rank] = w;
+  const int need = k - count([thr](uint32_t x) { return x > thr; });   // >= 1 keys equal to thr
+  const uint64_t below = (1ull << lane) - 1ull;   // lanes holding lower ids
+  int eq_rank = 0;                                // equal keys at lower ids
+#pragma unroll
+  for (int i = 0; i < V; ++i) eq_rank += __popcll(__ballot(key[i] == thr) & below);
+  bool chosen[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const bool eq = key[i] == thr;
+    chosen[i] = key[i] > thr || (eq && eq_rank < need);
+    eq_rank += eq;
+  }
+  int pos = 0;   // chosen experts at lower ids: this lane's first output slot
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    pos += __popcll(__ballot(chosen[i]) & below);
+    if (chosen[i]) part += s[i];
+  }
+  const float sum = wave_sum(part);
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      if (!chosen[i]) continue;
+      const float w = norm ? (s[i] / sum) * scale : s[i] * scale;
+      ids_out[static_cast<int64_t>(t) * k + pos] = lane * V + i;
+      w_out[static_cast<int64_t>(t) * k + pos] = w;
+      ++pos;
+    }
   }
 }
 
@@ -336,12 +358,17 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_topk(const RouterArgs& a, hipStream_t st) {
-  dim3 grid((a.T + 3) / 4), block(256);
+  const int topk_blocks = (a.T + 3) / 4;
+  // with x's fp8 codes: one quant block per 16 groups of 128 channels
+  const QuantSeg<uint16_t> xq{static_cast<const uint16_t*>(a.x), a.xq_codes ? a.T : 0, a.H, a.xq_codes,
+                              a.xq_scales};
+  const int64_t qblocks = (xq.R * (a.H / 128) + 15) / 16;
+  dim3 grid(static_cast<unsigned>(topk_blocks + qblocks)), block(256);
   const int V = (a.E + 63) / 64;
 #define MOE_TOPK(VV)                                                                         \
   hipLaunchKernelGGL(router_topk<VV>, grid, block, 0, st, a.logits, router_kparts(a.T, a.E, a.H, a.bf16), \
-                     a.bias, a.T, a.E, a.k,                                                   \
-                     a.n_group, a.topk_group, a.norm, a.scale, a.ids, a.w)
+                     a.bias, a.T, a.E, a.k, a.n_group, a.topk_group, a.norm, a.scale, a.ids, a.w,            \
+                     topk_blocks, xq)
   if (V <= 1) MOE_TOPK(1);
   else if (V <= 2) MOE_TOPK(2);
   else if (V <= 4) MOE_TOPK(4);
