@@ -231,6 +231,33 @@ def test_k2_decode_full_size(k2_weights, T):
     check_every_row(wl, case, out, ids, w)
 
 
+def test_k2_one_token_layer_equals_stage_chain(k2_weights):
+    """One token (T = 1, the smallest decode batch): for four different
+    tokens the fused layer equals route -> permute -> expert FFN -> combine
+    bit for bit and matches the oracle; so does the sub-block (RMSNorm,
+    layer, residual)."""
+    wl = W["k2_decode_bf16"]
+    for b in range(4):
+        x = cases.enforce_gap(wl, gen.gen_x(wl, 1, batch=10 + b), gen.gen_router(wl), gen.gen_bias(wl))
+        case = full_case(wl, k2_weights, 1)
+        case["x"] = x.cuda()
+        out, ids, w = run_layer(wl, case)
+        r = run_stages(wl, case)
+        same = torch.equal(out, r["out"]) and torch.equal(ids, r["ids"])
+        ref, route = cases.oracle_forward(wl, case)
+        say(f"  token {b}: layer == stage chain: {same}, rel err {rel_err(out, ref):.3e}")
+        assert same
+        check_route(ids, w, route)
+        assert rel_err(out, ref) <= TOL[wl.weight_dtype]
+    case = full_block_case(wl, k2_weights, 1)
+    out, ids, w = run_block(wl, case)
+    ref, route, _ = cases.oracle_block(wl, case)
+    check_route(ids, w, route)
+    err = block_err(out, ref, cases.to64(case["x"]), wl.act_dtype)
+    say(f"  sub-block, one token: err {err:.3e}")
+    assert err <= TOL[wl.weight_dtype]
+
+
 def check_grouped_rows(wl, case, r, route, hidden=None):
     """Stage chain at full size: grouping exact; every grouped row of every
     expert (y_perm) against the oracle's expert on that row; every shared row;
