@@ -444,10 +444,11 @@ def layer_roofline(wl, T, n_active, ms, routed_rows=None):
             "binding": "hbm" if t_b >= t_f else "mfma", "binding_frac": round(max(t_b, t_f) / sec, 4)}
 
 
-def sweep(args, wl, case, cfg, weights, hip):
-    """Decode sweep over token counts on the same resident weights; one JSON
-    record per point (tokens/s, time per step, active experts, fraction of
-    8 TB/s for the whole layer's algorithmic bytes)."""
+def sweep(args, wl, case, cfg, weights, hip, ceilings=None):
+    """Sweep over token counts on the same resident weights; one JSON record
+    per point (tokens/s, time per step, active experts, the whole layer's
+    fractions of 8 TB/s and of the dtype's MFMA peak, and the two grouped
+    GEMMs' rooflines, each also against the measured ceilings when given)."""
     recs = []
     for T in [int(t) for t in args.sweep_tokens.split(",")]:
         c = dict(case)
@@ -461,8 +462,12 @@ def sweep(args, wl, case, cfg, weights, hip):
                "layer_bytes": by, "layer_hbm_frac": round(by / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
                "layer_mfma_frac": lr["mfma_frac"], "binding": lr["binding"],
                "gate_up_ms": round(gu_ms, 4), "down_ms": round(LAST_DOWN_MS, 4),
-               "gate_up_roofline": roofline(wl, T, n_act, gu_ms, None),
-               "down_roofline": roofline(wl, T, n_act, LAST_DOWN_MS, None, kernel="down")}
+               "gate_up_roofline": with_measured(roofline(wl, T, n_act, gu_ms, None), ceilings),
+               "down_roofline": with_measured(roofline(wl, T, n_act, LAST_DOWN_MS, None, kernel="down"), ceilings)}
+        if ceilings:
+            peak = ceilings["mfma_fp8_loop_tflops" if wl.weight_dtype == gen.FP8 else "mfma_bf16_loop_tflops"]
+            rec["layer_mfma_frac_measured"] = round(layer_flops(wl, T) / (ms * 1e-3) / 1e12 / peak, 4)
+            rec["layer_hbm_frac_measured"] = round(by / (ms * 1e-3) / 1e9 / ceilings["hbm_read_gbs"], 4)
         print(f"[sweep] {json.dumps(rec)}", file=sys.stderr)
         recs.append(rec)
     return recs
@@ -634,7 +639,7 @@ def main():
                              row_capacity_per_token=cap)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, case, T, args.cpu_budget)
-    recs = sweep(args, wl, case, cfg, weights, hip) if args.sweep_tokens else []
+    recs = sweep(args, wl, case, cfg, weights, hip, ceilings) if args.sweep_tokens else []
     if args.extra_out:
         with open(args.extra_out, "a") as f:
             f.write(json.dumps({**res, "breakdown_ms": detail, "kernel_hash": kernel_hash()}) + "\n")
