@@ -227,6 +227,56 @@ def stored_traffic(workload: str, num_tokens: int):
     return d.get("traffic_bytes")
 
 
+# the gate_up kernel of each bench workload, and the sources its code comes from
+GATE_UP_KERNEL = {"k2_decode_bf16": ("gate_up_stream_bf16<", ["ffn_stream.hip", "common.h"]),
+                  "k2_prefill_bf16_zipf": ("ffn_tile_bf16<0,", ["ffn_tile.hip", "common.h"]),
+                  "k2_fp8": ("ffn_tile_fp8<0,", ["ffn_tile_fp8.hip", "common.h"])}
+
+
+def counter_means(run_dir: str, counter: str) -> dict:
+    """Mean value per dispatch of one rocprofv3 counter, per kernel name, from
+    the counter_collection.csv files of a `rocprofv3 --pmc <counter>
+    --output-format csv -d <run_dir>` run."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), max(v)) for k, v in vals.items()}
+
+
+def write_traffic(workload: str, num_tokens: int, fetch_dir: str, write_dir: str) -> dict:
+    """profiles/traffic_gate_up_<workload>.json from a FETCH_SIZE and a
+    WRITE_SIZE pass of `bench.py --workload <workload> --calib-copy` (KiB per
+    dispatch): each counter is scaled by what it reads for the 1 GiB device
+    copy of the same run (gfx950's FETCH_SIZE reads half of the bytes moved),
+    and the gate_up kernel's scaled mean is its HBM traffic per launch."""
+    prefix, sources = GATE_UP_KERNEL[workload]
+    fetch, write = counter_means(fetch_dir, "FETCH_SIZE"), counter_means(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if not copy:
+        sys.exit("no 1 GiB copy in the FETCH_SIZE run (pass --calib-copy)")
+    gib_kib = float(1 << 20)
+    fscale = gib_kib / fetch[copy[0]][1]
+    wcopy = [k for k in write if "copyBuffer" in k]
+    wscale = gib_kib / write[wcopy[0]][1]
+    names = [k for k in fetch if prefix in k]
+    if len(names) != 1:
+        sys.exit(f"expected one {prefix} kernel in the counter run, found {names}")
+    name = names[0]
+    traffic = fetch[name][0] * 1024 * fscale + write[name][0] * 1024 * wscale
+    d = {"workload": workload, "num_tokens": num_tokens, "kernel": name, "traffic_bytes": int(round(traffic)),
+         "fetch_kib": round(fetch[name][0], 1), "write_kib": round(write[name][0], 1),
+         "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+         "sources": {f: source_hash(f) for f in sources}}
+    with open(os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.json"), "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    return d
+
+
 def cpu_baseline(wl, case, T, budget_s):
     """The fp64 oracle (as it stands) on a bounded sample of the same tokens."""
     import threadpoolctl
@@ -531,7 +581,14 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes")
     ap.add_argument("--ceilings-only", action="store_true", help="print the measured ceilings and exit")
+    ap.add_argument("--traffic-json", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="write profiles/traffic_gate_up_<workload>.json from the csv output of a FETCH_SIZE "
+                         "and a WRITE_SIZE rocprofv3 pass of this workload (with --calib-copy), then exit")
     args = ap.parse_args()
+    if args.traffic_json:
+        wl = gen.WORKLOADS[args.workload]
+        print(json.dumps(write_traffic(args.workload, args.tokens or wl.num_tokens, *args.traffic_json)))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer runs unsharded on a single MI355X)",

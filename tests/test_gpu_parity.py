@@ -81,6 +81,18 @@ SMALL = [
                              num_experts_per_tok=6), 100),
     (W["small_bf16"].replace(name="small_bf16_nonorm", norm_topk_prob=False, routed_scaling_factor=1.0), 100),
     (W["small_fp8"].replace(name="small_fp8_noshared", n_shared_experts=0), 50),
+    # routing variants at decode sizes (the single-block grouping and work
+    # list): grouped routing, k = 32, E = 1023 (16 experts per lane), no
+    # renormalisation, fp8 with and without the shared expert
+    (W["small_grouped_bf16"], 16),
+    (W["small_bf16"].replace(name="small_bf16_g64", n_routed_experts=128, n_group=64, topk_group=3,
+                             num_experts_per_tok=6), 3),
+    (W["small_bf16"].replace(name="small_bf16_k32", n_routed_experts=64, num_experts_per_tok=32), 16),
+    (W["small_bf16"].replace(name="small_bf16_e1023", n_routed_experts=1023, hidden_size=256,
+                             moe_intermediate_size=128), 9),
+    (W["small_bf16"].replace(name="small_bf16_nonorm", norm_topk_prob=False, routed_scaling_factor=1.0), 2),
+    (W["small_fp8"], 16),
+    (W["small_fp8"].replace(name="small_fp8_noshared", n_shared_experts=0), 5),
 ]
 
 
