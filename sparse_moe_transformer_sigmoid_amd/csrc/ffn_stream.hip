@@ -400,7 +400,7 @@ FfnPlan ffn_plan(const FfnArgs& a, int weight_dtype, int act_dtype) {
   // (T=512: 2.85 ms against 3.05 tiled) but not 64-row ones (T=640: 4.00
   // against 3.12).
   if (weight_dtype == MOE_FP8_E4M3) {
-    if (per_expert >= 12.0 && tile_fp8_shapes_ok(a.H, a.F, a.Fs)) {
+    if (per_expert >= 12.0 && tile_fp8_shapes_ok(a.T, a.k, a.H, a.F, a.Fs)) {
       FfnPlan p{tile_fp8_rows(), FfnPlan::kTiled};
       p.w_once = per_expert <= 64.0;   // as for bf16 below (gate_up only: K2 fp8 T=512 layer 3.15 -> 3.10 ms)
       return p;

@@ -35,18 +35,27 @@ constexpr int kXcd = 8;
 // tracks it nor places its own (full) waits for it: every wait on these
 // loads is an explicit s_waitcnt vmcnt(n) below.  The instruction has no
 // register result (lane i writes 16 or 4 bytes at LDS address m0 + 16 i or
-// m0 + 4 i); its address operand is read at issue.
+// m0 + 4 i); its address operands are read at issue.  SADDR form: a
+// wave-uniform 64-bit base in SGPRs plus a 32-bit lane byte offset.
 template <bool NT = false>
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+__device__ __forceinline__ void dma16(uint64_t base, uint32_t voff, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
   if (NT)
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(m0v), "v"(g) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
   else
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+__device__ __forceinline__ void dma4(uint64_t base, uint32_t voff, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0v), "v"(g) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0v), "v"(voff), "s"(base) : "memory", "m0");
+}
+// a wave-uniform pointer as a 64-bit SGPR base (each half through uint32_t:
+// readfirstlane returns int, which would sign-extend the low word)
+__device__ __forceinline__ uint64_t sbase(const void* p) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 // LDS byte address of a __shared__ object (an address-space cast)
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -112,7 +121,7 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
   // ---- weights: this wave's DMA fills LDS rows 32*wave + [0, 32) (4
   // instructions of 8 rows); the compute side reads rows 64*wm + [0, 64) ----
   int K, o0;
-  const uint8_t* wdma;
+  const uint8_t* wdma;               // wave-uniform: the first of the wave's 32 DMA rows
   const float* wsc[2];               // scale rows of the wave's two 32-row tiles
   int64_t KB;
   if (MODE == 0) {
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     const uint8_t* wu = static_cast<const uint8_t*>(sh ? a.sh_up : a.w_up) + wofs;
     // LDS rows 64 q + [0, 32) = gate features o0 + 32 q + ., + [32, 64) = up
     const int q = wave >> 1, half = wave & 1;
-    wdma = (half ? wu : wg) + static_cast<int64_t>(o0 + 32 * q + drow) * K;
+    wdma = (half ? wu : wg) + static_cast<int64_t>(o0 + 32 * q) * K;
     const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.F / 128) * KB) + ((o0 + 32 * wm) / 128) * KB;
     wsc[0] = (sh ? a.sh_s_gate : a.s_gate) + sofs;
     wsc[1] = (sh ? a.sh_s_up : a.s_up) + sofs;
@@ -135,26 +144,39 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     o0 = slab * kBW;
     const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.H * a.F;
     const uint8_t* wd = static_cast<const uint8_t*>(sh ? a.sh_down : a.w_down) + wofs;
-    wdma = wd + static_cast<int64_t>(o0 + 32 * wave + drow) * K;
+    wdma = wd + static_cast<int64_t>(o0 + 32 * wave) * K;
     const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.H / 128) * KB) + ((o0 + 64 * wm) / 128) * KB;
     wsc[0] = wsc[1] = (sh ? a.sh_s_down : a.s_down) + sofs;
   }
-  const int64_t rstride8 = static_cast<int64_t>(8) * K;
-  // ---- grouped rows: this wave's DMA fills LDS rows kBW + 16*wave + [0, 16) ----
-  const uint8_t* xb[2];
+  const uint64_t wbase = sbase(wdma);
+  // lane offset of weight DMA instruction g (rows 8 g + drow of the wave's 32)
+  uint32_t woff[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) woff[g] = static_cast<uint32_t>((8 * g + drow) * K + dch[g & 1] * 16);
+  // ---- grouped rows: this wave's DMA fills LDS rows kBW + 16*wave + [0, 16);
+  // lane offsets from the (wave-uniform) start of the code rows: token * H
+  // (gathered routed rows), else the row index * row length (under 2^32
+  // bytes: tile_fp8_shapes_ok) ----
+  const uint8_t* xrow0;   // wave-uniform
+  if (MODE == 0)
+    xrow0 = sh ? static_cast<const uint8_t*>(a.xs) : static_cast<const uint8_t*>(a.xr);
+  else
+    xrow0 = sh ? static_cast<const uint8_t*>(a.hq_sh) : static_cast<const uint8_t*>(a.hq);
+  const uint64_t xbase = sbase(xrow0);
+  uint32_t xoff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int tr = 16 * wave + 8 * i + drow;
     const int64_t p = tl.row0 + min(tr, tl.rows - 1);
-    const uint8_t* base;
+    int64_t r, ld;
     if (MODE == 0) {
-      if (sh) base = static_cast<const uint8_t*>(a.xs) + (p - TK) * a.H;
-      else base = static_cast<const uint8_t*>(a.xr) + (a.xr_rows ? a.xr_rows[p] : p) * a.H;
+      r = sh ? p - TK : (a.xr_rows ? a.xr_rows[p] : p);
+      ld = a.H;
     } else {
-      base = sh ? static_cast<const uint8_t*>(a.hq_sh) + (p - TK) * a.Fs
-                : static_cast<const uint8_t*>(a.hq) + p * a.F;
+      r = sh ? p - TK : p;
+      ld = sh ? a.Fs : a.F;
     }
-    xb[i] = base + dch[i & 1] * 16;
+    xoff[i] = static_cast<uint32_t>(r * ld + dch[i & 1] * 16);
   }
   // ---- weight-block scales of the four 64-row groups, all K blocks, into
   // LDS once (read there at every step) ----
@@ -163,29 +185,34 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
   // ---- row scales: lane l of this wave copies the scale of grouped row
   // 16*wave + l % 16 for each step into the stage's 64 slots of the wave
   // (kData + 256 * wave + 4 * l; the compute side reads l < 16) ----
-  const float* rsd;
+  uint64_t rbase;   // wave-uniform start of the scale rows
+  uint32_t roff;    // this lane's row, in bytes
   {
     const int tr = 16 * wave + (lane & 15);
     const int64_t p = tl.row0 + min(tr, tl.rows - 1);
+    int64_t r;
+    const float* b;
     if (MODE == 0) {
-      if (sh) rsd = a.xs_scales + (p - TK) * KB;
-      else rsd = a.xr_scales + (a.xr_rows ? a.xr_rows[p] : p) * KB;
+      b = sh ? a.xs_scales : a.xr_scales;
+      r = sh ? p - TK : (a.xr_rows ? a.xr_rows[p] : p);
     } else {
-      rsd = sh ? a.h_sh_scales + (p - TK) * KB : a.h_scales + p * KB;
+      b = sh ? a.h_sh_scales : a.h_scales;
+      r = sh ? p - TK : p;
     }
+    rbase = sbase(b);
+    roff = static_cast<uint32_t>(r * KB * 4);
   }
-
   // the 7 DMA issues of step s into stage st: 4 x 8 weight rows, 2 x 8
   // grouped rows, then the 16 row scales
   auto dma = [&](int g, int s, const uint8_t* st) {
-    const int64_t ko = static_cast<int64_t>(s) * kRowB;
+    const uint32_t ko = static_cast<uint32_t>(s) * kRowB;
     const uint32_t l = lds_addr(st);
     if (g < 4) {
-      dma16<WNT>(wdma + g * rstride8 + ko + dch[g & 1] * 16, l + (32 * wave + 8 * g) * kRowB);
+      dma16<WNT>(wbase, woff[g] + ko, l + (32 * wave + 8 * g) * kRowB);
     } else if (g < 6) {
-      dma16(xb[g - 4] + ko, l + (kBW + 16 * wave + 8 * (g - 4)) * kRowB);
+      dma16(xbase, xoff[g - 4] + ko, l + (kBW + 16 * wave + 8 * (g - 4)) * kRowB);
     } else {
-      dma4(rsd + s, l + kData + 256 * wave);
+      dma4(rbase, roff + 4 * s, l + kData + 256 * wave);
     }
   };
 
@@ -358,9 +385,13 @@ int tile_fp8_rows() { return kBM; }
 
 // slabs must divide the weight dimensions, and every K fits the LDS table of
 // weight-block scales
-bool tile_fp8_shapes_ok(int H, int F, int Fs) {
+bool tile_fp8_shapes_ok(int64_t T, int k, int H, int F, int Fs) {
+  // DMA lane offsets are 32-bit: x codes (T rows of H), h codes (T k routed
+  // rows of F, T shared rows of Fs), row scales (per 128 channels)
+  const int64_t lim = 0xffffffffLL;
   return F % (kBW / 2) == 0 && Fs % (kBW / 2) == 0 && H % kBW == 0 && H <= 128 * kMaxKB &&
-         F <= 128 * kMaxKB && Fs <= 128 * kMaxKB;
+         F <= 128 * kMaxKB && Fs <= 128 * kMaxKB && T * H <= lim && T * k * F <= lim && T * Fs <= lim &&
+         T * k * (H / 128) * 4 <= lim && T * k * (F / 128) * 4 <= lim;
 }
 
 template <int MODE>

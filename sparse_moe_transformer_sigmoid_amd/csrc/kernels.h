@@ -158,5 +158,5 @@ namespace moe {
 hipError_t launch_gate_up_tile_fp8(const FfnArgs& a, hipStream_t st);
 hipError_t launch_down_tile_fp8(const FfnArgs& a, hipStream_t st);
 int tile_fp8_rows();
-bool tile_fp8_shapes_ok(int H, int F, int Fs);
+bool tile_fp8_shapes_ok(int64_t T, int k, int H, int F, int Fs);
 }  // namespace moe
