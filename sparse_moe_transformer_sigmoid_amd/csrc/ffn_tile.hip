@@ -363,8 +363,10 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
 
 // Sum of the K-part partials of each grouped row in part order, then the
 // epilogue: SiLU(gate) * up to h (gate_up) or the output row to y (down).
-// One block per grouped row; routed rows past offsets[E] (unused capacity)
-// and rows of no group are skipped.
+// Block (x, y) = grouped row x, output columns [1024 y, 1024 (y + 1)) (one
+// float4 per thread), so that the few rows of a split launch still give the
+// chip many blocks; routed rows past offsets[E] (unused capacity) and rows of
+// no group are skipped.
 template <int MODE>
 __global__ __launch_bounds__(256) void ffn_split_finish(FfnArgs a, int ks) {
   const int64_t p = blockIdx.x;
@@ -374,7 +376,8 @@ __global__ __launch_bounds__(256) void ffn_split_finish(FfnArgs a, int ks) {
   const int Fg = sh ? a.Fs : a.F;
   const int width = MODE == 0 ? 2 * max(a.F, a.Fs) : a.H;
   const int n4 = (MODE == 0 ? Fg : a.H) / 4;
-  for (int c = threadIdx.x; c < n4; c += blockDim.x) {
+  const int c = blockIdx.y * blockDim.x + threadIdx.x;
+  if (c < n4) {
     float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
     for (int kp = 0; kp < ks; ++kp) {
       const float* src = a.part + (static_cast<int64_t>(kp) * R + p) * width;
@@ -466,7 +469,9 @@ static hipError_t launch_tile(const FfnArgs& a, int slabs, int ks, hipStream_t s
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1) return e;
   const int64_t rows = static_cast<int64_t>(a.T) * a.k + a.T;
-  hipLaunchKernelGGL((ffn_split_finish<MODE>), dim3(static_cast<unsigned>(rows)), dim3(256), 0, st, a, ks);
+  const int cols4 = (MODE == 0 ? std::max(a.F, a.Fs) : a.H) / 4;
+  hipLaunchKernelGGL((ffn_split_finish<MODE>), dim3(static_cast<unsigned>(rows), (cols4 + 255) / 256), dim3(256), 0,
+                     st, a, ks);
   return hipGetLastError();
 }
 
