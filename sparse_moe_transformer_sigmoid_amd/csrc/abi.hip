@@ -124,7 +124,7 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0
 // workspace layout (one layout serves every entry point)
 // --------------------------------------------------------------------------
 struct Layout {
-  size_t logits, ids, w, ccount, cbase, offsets, rows, inv, tiles, tcount, xq, xs, h, hq, hs, hsh,
+  size_t logits, ids, w, ccount, cbase, offsets, rows, inv, tiles, tcount, xq, xs, xst, h, hq, hs, hsh,
       hqsh, hssh, y, ysh, u, part, total;
 };
 
@@ -156,6 +156,7 @@ Layout layout(const moe_config_t* c, int64_t T) {
   L.tcount = take(4);
   L.xq = take(fp8(c) ? T * H : 0);
   L.xs = take(fp8(c) ? T * (H / 128) * 4 : 0);
+  L.xst = take(fp8(c) ? (T * k + T) * (H / 128) * 4 : 0);
   L.h = take(T * k * F * hsz);
   L.hq = take(fp8(c) ? T * k * F : 0);
   L.hs = take(fp8(c) ? T * k * (F / 128) * 4 : 0);
@@ -317,6 +318,7 @@ moe_status_t run_ffn(const moe_config_t* c, const moe_weights_t* w, FfnArgs& f, 
   f.sh_s_gate = w->sh_s_gate;
   f.sh_s_up = w->sh_s_up;
   f.sh_s_down = w->sh_s_down;
+  f.xrs_t = fp8(c) ? at<float>(ws, layout(c, T).xst) : nullptr;
   TileArgs ta{};
   ta.offsets = f.offsets;
   ta.T = f.T;

@@ -185,22 +185,24 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
   // ---- row scales: lane l of this wave copies the scale of grouped row
   // 16*wave + l % 16 for each step into the stage's 64 slots of the wave
   // (kData + 256 * wave + 4 * l; the compute side reads l < 16) ----
+  // gate_up reads them K-block-major ([K block][grouped row], gathered by
+  // the same launch: a step's 16 rows are 64 contiguous bytes); down reads
+  // h's row-major scales ([row][K block])
   uint64_t rbase;   // wave-uniform start of the scale rows
   uint32_t roff;    // this lane's row, in bytes
+  uint32_t rstep;   // bytes from one K block to the next
   {
     const int tr = 16 * wave + (lane & 15);
     const int64_t p = tl.row0 + min(tr, tl.rows - 1);
-    int64_t r;
-    const float* b;
     if (MODE == 0) {
-      b = sh ? a.xs_scales : a.xr_scales;
-      r = sh ? p - TK : (a.xr_rows ? a.xr_rows[p] : p);
+      rbase = sbase(a.xrs_t);
+      roff = static_cast<uint32_t>(p * 4);
+      rstep = static_cast<uint32_t>((TK + a.T) * 4);
     } else {
-      b = sh ? a.h_sh_scales : a.h_scales;
-      r = sh ? p - TK : p;
+      rbase = sbase(sh ? a.h_sh_scales : a.h_scales);
+      roff = static_cast<uint32_t>((sh ? p - TK : p) * KB * 4);
+      rstep = 4;
     }
-    rbase = sbase(b);
-    roff = static_cast<uint32_t>(r * KB * 4);
   }
   // the 7 DMA issues of step s into stage st: 4 x 8 weight rows, 2 x 8
   // grouped rows, then the 16 row scales
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     } else if (g < 6) {
       dma16(xbase, xoff[g - 4] + ko, l + (kBW + 16 * wave + 8 * (g - 4)) * kRowB);
     } else {
-      dma4(rbase, roff + 4 * s, l + kData + 256 * wave);
+      dma4(rbase, roff + rstep * static_cast<uint32_t>(s), l + kData + 256 * wave);
     }
   };
 
@@ -381,6 +383,28 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
   }
 }
 
+// The row scales of the grouped rows of the tiled fp8 gate_up in
+// K-block-major order: st[kb][p] = the scale of grouped row p's activation
+// row in K block kb (routed rows p < T k through the row -> token map, shared
+// row T k + t = token t).  A thread per grouped row, so the writes of one K
+// block are contiguous across the block; routed rows past offsets[E] (unused
+// capacity) are skipped.
+__global__ __launch_bounds__(256) void gather_scales_t(FfnArgs a) {
+  const int64_t TK = static_cast<int64_t>(a.T) * a.k, R = TK + a.T;
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (p >= R) return;
+  const int KB = a.H / 128;
+  const float* src;
+  if (p < TK) {
+    if (p >= a.offsets[a.E]) return;
+    src = a.xr_scales + static_cast<int64_t>(a.xr_rows ? a.xr_rows[p] : p) * KB;
+  } else {
+    if (a.Fs == 0) return;
+    src = a.xs_scales + (p - TK) * KB;
+  }
+  for (int kb = 0; kb < KB; ++kb) a.xrs_t[kb * R + p] = src[kb];
+}
+
 int tile_fp8_rows() { return kBM; }
 
 // slabs must divide the weight dimensions, and every K fits the LDS table of
@@ -391,7 +415,7 @@ bool tile_fp8_shapes_ok(int64_t T, int k, int H, int F, int Fs) {
   const int64_t lim = 0xffffffffLL;
   return F % (kBW / 2) == 0 && Fs % (kBW / 2) == 0 && H % kBW == 0 && H <= 128 * kMaxKB &&
          F <= 128 * kMaxKB && Fs <= 128 * kMaxKB && T * H <= lim && T * k * F <= lim && T * Fs <= lim &&
-         T * k * (H / 128) * 4 <= lim && T * k * (F / 128) * 4 <= lim;
+         (T * k + T) * (H / 128) * 4 <= lim && T * k * (F / 128) * 4 <= lim;
 }
 
 template <int MODE>
@@ -411,8 +435,14 @@ static hipError_t launch_tile_fp8(const FfnArgs& a, int slabs, hipStream_t st) {
   return hipGetLastError();
 }
 
-// gate_up writes h already quantised (e4m3 codes + per-128 scales)
+// gate_up writes h already quantised (e4m3 codes + per-128 scales); its row
+// scales are gathered into K-block-major order first
 hipError_t launch_gate_up_tile_fp8(const FfnArgs& a, hipStream_t st) {
+  if (a.xrs_t == nullptr || a.offsets == nullptr) return hipErrorInvalidValue;
+  const int64_t R = static_cast<int64_t>(a.T) * a.k + a.T;
+  hipLaunchKernelGGL(gather_scales_t, dim3(static_cast<unsigned>((R + 255) / 256)), dim3(256), 0, st, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   return launch_tile_fp8<0>(a, std::max(a.F, a.Fs) / (kBW / 2), st);
 }
 

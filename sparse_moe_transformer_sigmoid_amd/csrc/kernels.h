@@ -94,6 +94,10 @@ struct FfnArgs {
   const int32_t* xr_rows;
   const void* xs;
   const float* xs_scales;
+  // fp8 tiled gate_up: workspace for the row scales of all grouped rows in
+  // K-block-major order [H/128][T*k + T] (gathered by the gate_up launch), or
+  // null
+  float* xrs_t;
   // SwiGLU output: routed [T*k][F], shared [T][Fs] (act dtype; fp32 for fp8
   // weights, then quantised into hq / hq_sh codes with per-128 scales)
   void* h;
