@@ -507,14 +507,18 @@ def test_k2_block_fp8_full_size(k2_fp8_weights):
 
 
 # ----------------------------------------------------------- graph capture --
-@pytest.mark.parametrize("name,block", [("small_bf16", False), ("small_fp8", False), ("small_bf16", True)])
-def test_layer_replays_from_a_graph(name, block):
+# 100 tokens: the tiled kernels; 8 tokens: the streaming kernels, bf16 and
+# fp8 (x quantised by the top-k launch, or by the norm pass of the block)
+@pytest.mark.parametrize("name,block,T", [("small_bf16", False, 100), ("small_fp8", False, 100),
+                                          ("small_bf16", True, 100), ("small_bf16", False, 8),
+                                          ("small_fp8", False, 8), ("small_bf16", True, 8),
+                                          ("small_fp8", True, 8)])
+def test_layer_replays_from_a_graph(name, block, T):
     """The entry points launch kernels only (no memset, no host sync), so a
     call can be captured in a HIP graph: every replay -- with eager library
     calls and a change of input between replays -- equals the eager result
     on the same input, bit for bit."""
     wl = W[name]
-    T = 100
     case = cases.make_block_case(wl, device="cuda", num_tokens=T) if block else small_case(wl, T)
     cfg = B.MoeConfig.from_fields(wl.fields())
     weights = B.MoeWeights.from_tensors(case)
