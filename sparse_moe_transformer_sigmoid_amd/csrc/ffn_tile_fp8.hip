@@ -6,13 +6,13 @@
 // Data movement as in the bf16 tile kernel -- both operands go global -> LDS
 // by DMA (global_load_lds_dwordx4), 128-byte unpadded LDS rows with the slot
 // swizzle chunk ^ ((row >> 1) & 7), XCD-chunked order of the work items --
-// but with three LDS stages, the DMA issued from inline asm and waited for
-// with counted s_waitcnt (the next step's DMA issues and the next row-tile's
-// LDS reads interleaved with the MFMAs).  A 128-byte row is 128 fp8
-// K-elements: exactly one quantisation block per K step, so each step is two
-// v_mfma_scale_f32_32x32x64_f8f6f4 (unit e8m0 scales) per 32x32 output tile
-// into a fresh partial, added to the fp32 accumulator scaled by weight-block
-// scale x row scale:
+// but with separate LDS rings for the weight rows (six stages, each half of
+// a step's rows) and the grouped rows (three stages), the DMA issued from
+// inline asm and waited for with counted s_waitcnt.  A 128-byte row is 128
+// fp8 K-elements: exactly one quantisation block per K step, so each step is
+// two v_mfma_scale_f32_32x32x64_f8f6f4 (unit e8m0 scales) per 32x32 output
+// tile into a fresh partial, added to the fp32 accumulator scaled by
+// weight-block scale x row scale:
 //   acc += (sum_k q_w q_a) * s_w[block][kb] * s_a[row][kb].
 // The block is 256 weight rows x 128 grouped rows in 8 waves of 64 x 64.
 // gate_up writes the SwiGLU output already quantised for the down projection
@@ -26,8 +26,9 @@ namespace {
 constexpr int kBM = 128;                      // grouped rows per work item
 constexpr int kBW = 256;                      // weight rows per slab
 constexpr int kRowB = 128;                    // bytes per LDS row = K elements per step
-constexpr int kData = (kBW + kBM) * kRowB;    // 48 KB of operands per stage
-constexpr int kStage = kData + 8 * 64 * 4;     // + grouped-row scales: 64 slots per wave
+constexpr int kWStage = (kBW / 2) * kRowB;    // 16 KB: one half of a step's weight rows
+constexpr int kXData = kBM * kRowB;           // 16 KB: a step's grouped rows
+constexpr int kXStage = kXData + 8 * 64 * 4;  // + their row scales: 64 slots per wave
 constexpr int kMaxKB = 64;                     // K blocks (K <= 8192) of the weight-scale table
 constexpr int kXcd = 8;
 
@@ -77,19 +78,28 @@ __device__ __forceinline__ f32x16 mma_fp8_32(const uint4& a0, const uint4& a1, c
 
 // MODE 0: gate_up (K = H; slab = 128 features = 128 gate + 128 up rows)
 // MODE 1: down    (K = F or Fs; slab = 256 output rows)
-// 8 waves, two per SIMD: wave (wm, wn) owns LDS weight rows 64*wm + [0, 64)
-// (gate_up: 32 gate then 32 up rows of features o0 + 32*wm + [0, 32)) and
-// grouped rows 64*wn + [0, 64); while one wave of a SIMD applies the scales
-// of its partial products (VALU), the other's MFMAs run.
+// A K step (one 128-wide quantisation block) is taken in two halves, each
+// over one half of the slab's weight rows (gate_up: the gate rows, then the
+// up rows; down: output rows o0 + [0, 128), then o0 + 128 + [0, 128)) and
+// all 128 grouped rows.  The weight halves stream through a ring of six
+// 16 KB stages (the DMA of half h + 5 is issued during half h, so five
+// halves -- 80 KB of weights -- are in flight per block), the grouped rows
+// through a ring of three 16 KB stages (+ their row scales; the DMA of step
+// s + 2 during step s).  8 waves, two per SIMD: wave (wm, wn) owns weight
+// rows 32*wm + [0, 32) of each half (gate_up: gate then up rows of features
+// o0 + 32*wm + [0, 32)) and grouped rows 64*wn + [0, 64); while one wave of
+// a SIMD applies the scales of its partial products (VALU), the other's
+// MFMAs run.
 // WNT: the weight DMA carries the nontemporal hint (each weight slab is
 // expected to be read by one tile only)
 template <int MODE, bool WNT>
 __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
-  // three stages as separate objects
-  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t st1[kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[kStage];
-  __shared__ float wscale[4][2][kMaxKB];        // [wm][gate/up or down][K block]
+  // the rings as separate objects (compile-time LDS addresses)
+  __shared__ __attribute__((aligned(16))) uint8_t ws0[kWStage], ws1[kWStage], ws2[kWStage], ws3[kWStage],
+      ws4[kWStage], ws5[kWStage];
+  __shared__ __attribute__((aligned(16))) uint8_t xs0[kXStage], xs1[kXStage], xs2[kXStage];
+  __shared__ float wscale[4 * kBM];   // [half][K block] (kMaxKB each); the epilogue's row maxima
+  static_assert(2 * kMaxKB <= 4 * kBM, "weight-scale table fits");
   const int ntile = *a.tile_count;
   const int total = slabs * ntile;
   const int per = (total + kXcd - 1) / kXcd;
@@ -113,16 +123,16 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
   const int Fg = sh ? a.Fs : a.F;
   const int64_t TK = static_cast<int64_t>(a.T) * a.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;        // 64 weight rows x 64 grouped rows
+  const int wm = wave >> 1, wn = wave & 1;        // 32 weight rows (per half) x 64 grouped rows
   const int r32 = lane & 31, kh = lane >> 5;
   const int drow = lane >> 3;
   const int dch[2] = {(lane & 7) ^ ((drow >> 1) & 7), (lane & 7) ^ ((4 + (drow >> 1)) & 7)};
 
-  // ---- weights: this wave's DMA fills LDS rows 32*wave + [0, 32) (4
-  // instructions of 8 rows); the compute side reads rows 64*wm + [0, 64) ----
+  // ---- weights: this wave's DMA fills rows 16*wave + [0, 16) of each half
+  // (2 instructions of 8 rows); the compute side reads rows 32*wm + [0, 32) ----
   int K, o0;
-  const uint8_t* wdma;               // wave-uniform: the first of the wave's 32 DMA rows
-  const float* wsc[2];               // scale rows of the wave's two 32-row tiles
+  const uint8_t* wdma[2];            // wave-uniform: the first of the wave's 16 DMA rows, per half
+  const float* wsc[2];               // weight-block scale rows of the two halves
   int64_t KB;
   if (MODE == 0) {
     K = a.H;
@@ -132,10 +142,9 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.F * a.H;
     const uint8_t* wg = static_cast<const uint8_t*>(sh ? a.sh_gate : a.w_gate) + wofs;
     const uint8_t* wu = static_cast<const uint8_t*>(sh ? a.sh_up : a.w_up) + wofs;
-    // LDS rows 64 q + [0, 32) = gate features o0 + 32 q + ., + [32, 64) = up
-    const int q = wave >> 1, half = wave & 1;
-    wdma = (half ? wu : wg) + static_cast<int64_t>(o0 + 32 * q) * K;
-    const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.F / 128) * KB) + ((o0 + 32 * wm) / 128) * KB;
+    wdma[0] = wg + static_cast<int64_t>(o0 + 16 * wave) * K;
+    wdma[1] = wu + static_cast<int64_t>(o0 + 16 * wave) * K;
+    const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.F / 128) * KB) + (o0 / 128) * KB;
     wsc[0] = (sh ? a.sh_s_gate : a.s_gate) + sofs;
     wsc[1] = (sh ? a.sh_s_up : a.s_up) + sofs;
   } else {
@@ -144,19 +153,23 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     o0 = slab * kBW;
     const int64_t wofs = sh ? 0 : static_cast<int64_t>(tl.group) * a.H * a.F;
     const uint8_t* wd = static_cast<const uint8_t*>(sh ? a.sh_down : a.w_down) + wofs;
-    wdma = wd + static_cast<int64_t>(o0 + 32 * wave) * K;
-    const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.H / 128) * KB) + ((o0 + 64 * wm) / 128) * KB;
-    wsc[0] = wsc[1] = (sh ? a.sh_s_down : a.s_down) + sofs;
+    wdma[0] = wd + static_cast<int64_t>(o0 + 16 * wave) * K;
+    wdma[1] = wd + static_cast<int64_t>(o0 + kBW / 2 + 16 * wave) * K;
+    const int64_t sofs = (sh ? 0 : static_cast<int64_t>(tl.group) * (a.H / 128) * KB) + (o0 / 128) * KB;
+    wsc[0] = (sh ? a.sh_s_down : a.s_down) + sofs;
+    wsc[1] = wsc[0] + KB;
   }
-  const uint64_t wbase = sbase(wdma);
-  // lane offset of weight DMA instruction g (rows 8 g + drow of the wave's 32)
-  uint32_t woff[4];
+  // (two scalars, not an array: a select between array elements became a
+  // dynamically indexed array, which the compiler placed in LDS)
+  const uint64_t wbase0 = sbase(wdma[0]), wbase1 = sbase(wdma[1]);
+  // lane offset of weight DMA instruction g (rows 8 g + drow of the wave's 16)
+  uint32_t woff[2];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) woff[g] = static_cast<uint32_t>((8 * g + drow) * K + dch[g & 1] * 16);
-  // ---- grouped rows: this wave's DMA fills LDS rows kBW + 16*wave + [0, 16);
-  // lane offsets from the (wave-uniform) start of the code rows: token * H
-  // (gathered routed rows), else the row index * row length (under 2^32
-  // bytes: tile_fp8_shapes_ok) ----
+  for (int g = 0; g < 2; ++g) woff[g] = static_cast<uint32_t>((8 * g + drow) * K + dch[g] * 16);
+  // ---- grouped rows: this wave's DMA fills rows 16*wave + [0, 16) of a
+  // grouped-row stage; lane offsets from the (wave-uniform) start of the code
+  // rows: token * H (gathered routed rows), else the row index * row length
+  // (under 2^32 bytes: tile_fp8_shapes_ok) ----
   const uint8_t* xrow0;   // wave-uniform
   if (MODE == 0)
     xrow0 = sh ? static_cast<const uint8_t*>(a.xs) : static_cast<const uint8_t*>(a.xr);
@@ -176,15 +189,17 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
       r = sh ? p - TK : p;
       ld = sh ? a.Fs : a.F;
     }
-    xoff[i] = static_cast<uint32_t>(r * ld + dch[i & 1] * 16);
+    xoff[i] = static_cast<uint32_t>(r * ld + dch[i] * 16);
   }
-  // ---- weight-block scales of the four 64-row groups, all K blocks, into
-  // LDS once (read there at every step) ----
-  if (wn == 0)
-    for (int i = lane; i < 2 * KB; i += 64) wscale[wm][i / KB][i % KB] = wsc[i / KB][i % KB];
+  // ---- weight-block scales of the two halves, all K blocks, into LDS once
+  // (read there at every half step) ----
+  for (int i = tid; i < KB; i += 512) {
+    wscale[i] = wsc[0][i];
+    wscale[kMaxKB + i] = wsc[1][i];
+  }
   // ---- row scales: lane l of this wave copies the scale of grouped row
   // 16*wave + l % 16 for each step into the stage's 64 slots of the wave
-  // (kData + 256 * wave + 4 * l; the compute side reads l < 16) ----
+  // (kXData + 256 * wave + 4 * l; the compute side reads l < 16) ----
   // gate_up reads them K-block-major ([K block][grouped row], gathered by
   // the same launch: a step's 16 rows are 64 contiguous bytes); down reads
   // h's row-major scales ([row][K block])
@@ -204,21 +219,29 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
       rstep = 4;
     }
   }
-  // the 7 DMA issues of step s into stage st: 4 x 8 weight rows, 2 x 8
-  // grouped rows, then the 16 row scales
-  auto dma = [&](int g, int s, const uint8_t* st) {
+  const int steps = static_cast<int>(KB), halves = 2 * steps;
+  // the DMA of weight half hh (step hh / 2, half hh % 2; clamped to the last
+  // one, whose data then lands in a stage nobody reads again): 2 issues
+  auto dma_w = [&](int hh, uint8_t* st) {
+    hh = min(hh, halves - 1);
+    const uint32_t ko = static_cast<uint32_t>(hh >> 1) * kRowB;
+    const uint32_t l = lds_addr(st) + 16 * wave * kRowB;
+    const uint64_t b = (hh & 1) ? wbase1 : wbase0;
+    dma16<WNT>(b, woff[0] + ko, l);
+    dma16<WNT>(b, woff[1] + ko, l + 8 * kRowB);
+  };
+  // the DMA of the grouped rows of step s (clamped likewise): 2 row issues,
+  // then the 16 row scales
+  auto dma_x = [&](int s, uint8_t* st) {
+    s = min(s, steps - 1);
     const uint32_t ko = static_cast<uint32_t>(s) * kRowB;
     const uint32_t l = lds_addr(st);
-    if (g < 4) {
-      dma16<WNT>(wbase, woff[g] + ko, l + (32 * wave + 8 * g) * kRowB);
-    } else if (g < 6) {
-      dma16(xbase, xoff[g - 4] + ko, l + (kBW + 16 * wave + 8 * (g - 4)) * kRowB);
-    } else {
-      dma4(rbase, roff + rstep * static_cast<uint32_t>(s), l + kData + 256 * wave);
-    }
+    dma16(xbase, xoff[0] + ko, l + (16 * wave) * kRowB);
+    dma16(xbase, xoff[1] + ko, l + (16 * wave + 8) * kRowB);
+    dma4(rbase, roff + rstep * static_cast<uint32_t>(s), l + kXData + 256 * wave);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][2];   // [half][grouped-row tile]
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -226,82 +249,95 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.f;
 
-  const int steps = static_cast<int>(KB);
   const int sw = (r32 >> 1) & 7;
-  const int arow = (64 * wm + r32) * kRowB;
-  const int brow = (kBW + 64 * wn + r32) * kRowB;
-  // grouped row r = 64 wn + 32 n + r32 has its scale at kData + 256 (r / 16) + 4 (r % 16)
-  const int srow = kData + 256 * (4 * wn + (r32 >> 4)) + 4 * (r32 & 15);
+  const int arow = (32 * wm + r32) * kRowB;
+  const int brow = (64 * wn + r32) * kRowB;
+  // grouped row r = 64 wn + 32 n + r32 has its scale at kXData + 256 (r / 16) + 4 (r % 16)
+  const int srow = kXData + 256 * (4 * wn + (r32 >> 4)) + 4 * (r32 & 15);
   // fragments of one 32-row tile: MFMA i (0, 1) takes chunks kh*4 + 2i, +1
   auto frag = [&](const uint8_t* st, int row, uint4 (&f)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) f[c] = *reinterpret_cast<const uint4*>(st + row + (((kh * 4 + c) ^ sw) * 16));
   };
-  // One K step s (one 128-wide quantisation block) on stage rd while the DMA
-  // of step sd (= s + 2, clamped) fills stage wr: the four 32x32 tiles t =
-  // (m, n), the partial product of tile t+1 computed before tile t's is
-  // scaled into the accumulator (MFMA and VALU work overlap).
-  auto step = [&](const uint8_t* rd, const uint8_t* wr, int s, int sd) {
-    const float ws[2] = {wscale[wm][0][s], wscale[wm][1][s]};
-    const float rs[2] = {*reinterpret_cast<const float*>(rd + srow),
-                         *reinterpret_cast<const float*>(rd + srow + 512)};
-    uint4 af[2][4], bf[2][4];
-    frag(rd, arow, af[0]);
-    frag(rd, arow + 32 * kRowB, af[1]);
-    frag(rd, brow, bf[0]);
-    frag(rd, brow + 32 * kRowB, bf[1]);
+  // One half step: weight half h of step s from stage w against the grouped
+  // rows' fragments bf (read from the step's stage in the first half, kept
+  // in registers for the second); the partial product of tile 1 is computed
+  // before tile 0's is scaled into the accumulator (MFMA and VALU overlap).
+  // issue() runs the half step's DMA between them.  Then the counted wait:
+  // at most `keep` of this wave's DMA issues may still be outstanding (those
+  // of the last four half steps that the next half step does not read), and
+  // this wave's LDS reads are done (lgkmcnt); then the barrier.
+  auto half = [&](const uint8_t* w, int h, int s, const uint4 (&bf)[2][4], const float (&rs)[2], auto issue,
+                  auto keep) {
+    const float ws = wscale[h * kMaxKB + s];
+    uint4 af[4];
+    frag(w, arow, af);
     f32x16 p[2];
-    auto part = [&](int t) {
-      const int m = t >> 1, n = t & 1;
+    auto part = [&](int n) {
       f32x16 z;
 #pragma unroll
       for (int i = 0; i < 16; ++i) z[i] = 0.f;
-      z = mma_fp8_32(af[m][0], af[m][1], bf[n][0], bf[n][1], z);
-      p[t & 1] = mma_fp8_32(af[m][2], af[m][3], bf[n][2], bf[n][3], z);
+      z = mma_fp8_32(af[0], af[1], bf[n][0], bf[n][1], z);
+      p[n] = mma_fp8_32(af[2], af[3], bf[n][2], bf[n][3], z);
     };
-    auto fold = [&](int t) {
-      const int m = t >> 1, n = t & 1;
-      // gate_up: m = 0 gate rows, 1 up rows; down: one block
-      const float sc = ws[m] * rs[n];
+    auto fold = [&](int n) {
+      const float sc = ws * rs[n];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[m][n][i] = fmaf(p[t & 1][i], sc, acc[m][n][i]);
+      for (int i = 0; i < 16; ++i) acc[h][n][i] = fmaf(p[n][i], sc, acc[h][n][i]);
     };
     part(0);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < 3) part(t + 1);
-      dma(2 * t, sd, wr);
-      if (t < 3) dma(2 * t + 1, sd, wr);
-      fold(t);
-    }
-    // this wave's DMA of step s + 1 has landed once at most the 7 issued
-    // during this step are outstanding; this wave's LDS reads are done
-    // (lgkmcnt); then the barrier.  (__syncthreads would also wait for the
-    // DMA of step s + 2.)
-    // (fenced against the scheduler: nothing moves across the wait; K2 fp8
-    // T=4096 4.38 -> 4.34 ms, T=1024 3.25 -> 3.21)
+    part(1);
+    issue();
+    fold(0);
+    fold(1);
+    // (fenced against the scheduler: nothing moves across the wait)
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (decltype(keep)::value == 14)
+      asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
+  // One step s on grouped-row stage x and weight stages w0 (half 0), w1
+  // (half 1): the first half issues the grouped rows of step s + 2 (into xn,
+  // the stage of step s - 1) and weight half 2s + 5 (into wp, the stage of
+  // half 2s - 1); the second issues weight half 2s + 6 (into w0).  Waits:
+  // after the first half the next one needs weight half 2s + 1 (issued
+  // during half 2s - 4: 14 issues since); after the second, the next step
+  // needs weight half 2s + 2 and the grouped rows of step s + 1 (issued
+  // during half 2s - 2 before its 2 weight issues: 11 issues since).
+  auto step = [&](uint8_t* x, uint8_t* xn, uint8_t* w0, uint8_t* w1, uint8_t* wp, int s) {
+    uint4 bf[2][4];
+    frag(x, brow, bf[0]);
+    frag(x, brow + 32 * kRowB, bf[1]);
+    const float rs[2] = {*reinterpret_cast<const float*>(x + srow),
+                         *reinterpret_cast<const float*>(x + srow + 512)};
+    half(w0, 0, s, bf, rs, [&] { dma_x(s + 2, xn); dma_w(2 * s + 5, wp); },
+         std::integral_constant<int, 14>());
+    half(w1, 1, s, bf, rs, [&] { dma_w(2 * s + 6, w0); }, std::integral_constant<int, 11>());
+  };
 
-#pragma unroll
-  for (int g = 0; g < 7; ++g) dma(g, 0, st0);
-#pragma unroll
-  for (int g = 0; g < 7; ++g) dma(g, min(1, steps - 1), st1);
+  // as if issued by half steps -5 .. -1: weight halves 0..4 and the grouped
+  // rows of steps 0 and 1 (same order, so the same counted wait: the first
+  // step needs weight half 0 and grouped rows 0, 11 issues before the end)
+  dma_w(0, ws0);
+  dma_x(0, xs0);
+  dma_w(1, ws1);
+  dma_w(2, ws2);
+  dma_x(1, xs1);
+  dma_w(3, ws3);
+  dma_w(4, ws4);
   // (lgkmcnt: the weight-scale table written above is visible after the barrier)
-  asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  // steps in threes (stages 0, 1, 2); a DMA index past the end re-loads the
-  // last step's (in-bounds) data into a stage nobody reads again
-  const int last = steps - 1;
+  asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // steps in threes (grouped-row stages 0, 1, 2; weight stages 0..5)
   int s = 0;
   for (; s + 2 < steps; s += 3) {
-    step(st0, st2, s, min(s + 2, last));
-    step(st1, st0, s + 1, min(s + 3, last));
-    step(st2, st1, s + 2, min(s + 4, last));
+    step(xs0, xs2, ws0, ws1, ws5, s);
+    step(xs1, xs0, ws2, ws3, ws1, s + 1);
+    step(xs2, xs1, ws4, ws5, ws3, s + 2);
   }
-  if (s < steps) step(st0, st2, s, min(s + 2, last));
-  if (s + 1 < steps) step(st1, st0, s + 1, min(s + 3, last));
+  if (s < steps) step(xs0, xs2, ws0, ws1, ws5, s);
+  if (s + 1 < steps) step(xs1, xs0, ws2, ws3, ws1, s + 1);
   // no DMA may still be writing LDS when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -316,8 +352,8 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     // the activation-quant kernel.  The row maxima meet in LDS, in the
     // weight-scale table: no DMA ever targets it (a stage may still receive a
     // refill that another wave issued in the last step, which only that
-    // wave's own vmcnt(0) above waits for), and the last step's barrier came
-    // after every wave's reads of the table (lgkmcnt(0)).
+    // wave's own vmcnt(0) above waits for), and the last half step's barrier
+    // came after every wave's reads of the table (lgkmcnt(0)).
     float hv[2][16], rmax[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -329,8 +365,7 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
       }
       rmax[n] = fmaxf(m, __shfl_xor(m, 32, 64));
     }
-    static_assert(sizeof(wscale) >= 4 * kBM * sizeof(float), "row maxima fit the scale table");
-    float* gmax = &wscale[0][0][0];   // [4 wm][128 rows]
+    float* gmax = wscale;   // [4 wm][128 rows]
     if (kh == 0) {
 #pragma unroll
       for (int n = 0; n < 2; ++n) gmax[128 * wm + 64 * wn + 32 * n + r32] = rmax[n];
@@ -360,7 +395,7 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     }
     return;
   }
-  // down: y in bf16
+  // down: y in bf16 (half m holds output rows o0 + 128 m + 32 wm + .)
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int tr = 64 * wn + 32 * n + r32;
@@ -368,7 +403,7 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     const int64_t p = tl.row0 + tr;
     uint16_t* dst = sh ? static_cast<uint16_t*>(a.y_sh) + (p - TK) * a.H
                        : static_cast<uint16_t*>(a.y) + p * a.H;
-    dst += o0 + 64 * wm + 4 * kh;
+    dst += o0 + 32 * wm + 4 * kh;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -378,7 +413,7 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
                (static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 1])) << 16);
         v2.y = static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 2])) |
                (static_cast<uint32_t>(f32_to_bf16(acc[m][n][4 * g + 3])) << 16);
-        *reinterpret_cast<uint2*>(dst + 32 * m + 8 * g) = v2;
+        *reinterpret_cast<uint2*>(dst + (kBW / 2) * m + 8 * g) = v2;
       }
   }
 }
