@@ -259,16 +259,28 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) f[c] = *reinterpret_cast<const uint4*>(st + row + (((kh * 4 + c) ^ sw) * 16));
   };
+  // The partial products of the previous half step and their scales: folded
+  // into that half's accumulators during the next half step, while its MFMAs
+  // run (the fold does not wait on them).  Each accumulator still takes its
+  // K blocks in order.  Before the first half step: zeros (a fold of 0 x 0).
+  f32x16 pp[2];
+  float psc[2] = {0.f, 0.f};
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pp[n][i] = 0.f;
   // One half step: weight half h of step s from stage w against the grouped
   // rows' fragments bf (read from the step's stage in the first half, kept
-  // in registers for the second); the partial product of tile 1 is computed
-  // before tile 0's is scaled into the accumulator (MFMA and VALU overlap).
-  // issue() runs the half step's DMA between them.  Then the counted wait:
-  // at most `keep` of this wave's DMA issues may still be outstanding (those
-  // of the last four half steps that the next half step does not read), and
-  // this wave's LDS reads are done (lgkmcnt); then the barrier.
-  auto half = [&](const uint8_t* w, int h, int s, const uint4 (&bf)[2][4], const float (&rs)[2], auto issue,
+  // in registers for the second): two 32x32 tiles' partial products, then
+  // the previous half step's partials folded into its accumulators (of half
+  // 1 - h) while these MFMAs run; issue() runs the half step's DMA between
+  // them.  Then the counted wait: at most `keep` of this wave's DMA issues
+  // may still be outstanding (those of the last four half steps that the
+  // next half step does not read), and this wave's LDS reads are done
+  // (lgkmcnt); then the barrier.
+  auto half = [&](const uint8_t* w, auto hc, int s, const uint4 (&bf)[2][4], const float (&rs)[2], auto issue,
                   auto keep) {
+    constexpr int h = decltype(hc)::value;
     const float ws = wscale[h * kMaxKB + s];
     uint4 af[4];
     frag(w, arow, af);
@@ -280,16 +292,18 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
       z = mma_fp8_32(af[0], af[1], bf[n][0], bf[n][1], z);
       p[n] = mma_fp8_32(af[2], af[3], bf[n][2], bf[n][3], z);
     };
-    auto fold = [&](int n) {
-      const float sc = ws * rs[n];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[h][n][i] = fmaf(p[n][i], sc, acc[h][n][i]);
-    };
     part(0);
     part(1);
     issue();
-    fold(0);
-    fold(1);
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[1 - h][n][i] = fmaf(pp[n][i], psc[n], acc[1 - h][n][i]);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      pp[n] = p[n];
+      psc[n] = ws * rs[n];
+    }
     // (fenced against the scheduler: nothing moves across the wait)
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(keep)::value == 14)
@@ -312,9 +326,10 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
     frag(x, brow + 32 * kRowB, bf[1]);
     const float rs[2] = {*reinterpret_cast<const float*>(x + srow),
                          *reinterpret_cast<const float*>(x + srow + 512)};
-    half(w0, 0, s, bf, rs, [&] { dma_x(s + 2, xn); dma_w(2 * s + 5, wp); },
+    half(w0, std::integral_constant<int, 0>(), s, bf, rs, [&] { dma_x(s + 2, xn); dma_w(2 * s + 5, wp); },
          std::integral_constant<int, 14>());
-    half(w1, 1, s, bf, rs, [&] { dma_w(2 * s + 6, w0); }, std::integral_constant<int, 11>());
+    half(w1, std::integral_constant<int, 1>(), s, bf, rs, [&] { dma_w(2 * s + 6, w0); },
+         std::integral_constant<int, 11>());
   };
 
   // as if issued by half steps -5 .. -1: weight halves 0..4 and the grouped
@@ -338,6 +353,11 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
   }
   if (s < steps) step(xs0, xs2, ws0, ws1, ws5, s);
   if (s + 1 < steps) step(xs1, xs0, ws2, ws3, ws1, s + 1);
+  // the last half step's partials (half 1)
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[1][n][i] = fmaf(pp[n][i], psc[n], acc[1][n][i]);
   // no DMA may still be writing LDS when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
