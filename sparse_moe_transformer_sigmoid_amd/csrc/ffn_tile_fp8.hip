@@ -89,36 +89,14 @@ __device__ __forceinline__ f32x16 mma_fp8_32(const uint4& a0, const uint4& a1, c
 // rows 32*wm + [0, 32) of each half (gate_up: gate then up rows of features
 // o0 + 32*wm + [0, 32)) and grouped rows 64*wn + [0, 64); while one wave of
 // a SIMD applies the scales of its partial products (VALU), the other's
-// MFMAs run.
-// WNT: the weight DMA carries the nontemporal hint (each weight slab is
-// expected to be read by one tile only)
+// MFMAs run.  WNT: the weight DMA carries the nontemporal hint.  The LDS
+// rings and table are the kernel's (one allocation for both copies of this
+// body that the kernel inlines).
 template <int MODE, bool WNT>
-__global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
-  // the rings as separate objects (compile-time LDS addresses)
-  __shared__ __attribute__((aligned(16))) uint8_t ws0[kWStage], ws1[kWStage], ws2[kWStage], ws3[kWStage],
-      ws4[kWStage], ws5[kWStage];
-  __shared__ __attribute__((aligned(16))) uint8_t xs0[kXStage], xs1[kXStage], xs2[kXStage];
-  __shared__ float wscale[4 * kBM];   // [half][K block] (kMaxKB each); the epilogue's row maxima
-  static_assert(2 * kMaxKB <= 4 * kBM, "weight-scale table fits");
-  const int ntile = *a.tile_count;
-  const int total = slabs * ntile;
-  const int per = (total + kXcd - 1) / kXcd;
-  const int j = blockIdx.x / kXcd;
-  const int v = (blockIdx.x % kXcd) * per + j;
-  if (j >= per || v >= total) return;
-  // gate_up: slab-major (the tiles of one weight slab side by side on an
-  // XCD); down: tile-major (the slabs of one tile side by side, so its h rows
-  // are fetched once per XCD).  Measured on the K2 fp8 layer, T = 512..8192:
-  // tile-major down 1-2 % faster, tile-major gate_up 4 % slower.
-  int slab, tix;
-  if (MODE == 1) {
-    tix = v / slabs;
-    slab = v - tix * slabs;
-  } else {
-    slab = v / ntile;
-    tix = v - slab * ntile;
-  }
-  const Tile tl = a.tiles[tix];
+__device__ __forceinline__ void tile_fp8_body(const FfnArgs& a, int slab, const Tile& tl, uint8_t* ws0,
+                                              uint8_t* ws1, uint8_t* ws2, uint8_t* ws3, uint8_t* ws4,
+                                              uint8_t* ws5, uint8_t* xs0, uint8_t* xs1, uint8_t* xs2,
+                                              float* wscale) {
   const bool sh = tl.group == a.E;
   const int Fg = sh ? a.Fs : a.F;
   const int64_t TK = static_cast<int64_t>(a.T) * a.k;
@@ -436,6 +414,39 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
         *reinterpret_cast<uint2*>(dst + (kBW / 2) * m + 8 * g) = v2;
       }
   }
+}
+
+// WNT: the weight DMA of routed tiles carries the nontemporal hint (each
+// routed weight slab is expected to be read by one tile only); never that
+// of the shared expert, whose slabs every token tile reads.  The block
+// branches once, on its tile, between two inlined copies of the pipeline (a
+// branch per DMA issue made the kernel spill).
+template <int MODE, bool WNT>
+__global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
+  // the rings as separate objects (compile-time LDS addresses)
+  __shared__ __attribute__((aligned(16))) uint8_t ws0[kWStage], ws1[kWStage], ws2[kWStage], ws3[kWStage],
+      ws4[kWStage], ws5[kWStage];
+  __shared__ __attribute__((aligned(16))) uint8_t xs0[kXStage], xs1[kXStage], xs2[kXStage];
+  __shared__ float wscale[4 * kBM];   // [half][K block] (kMaxKB each); the epilogue's row maxima
+  static_assert(2 * kMaxKB <= 4 * kBM, "weight-scale table fits");
+  const int ntile = *a.tile_count;
+  const int total = slabs * ntile;
+  const int per = (total + kXcd - 1) / kXcd;
+  const int j = blockIdx.x / kXcd;
+  const int v = (blockIdx.x % kXcd) * per + j;
+  if (j >= per || v >= total) return;
+  // tile-major: the slabs of one tile side by side on an XCD, so its
+  // grouped rows are fetched once per XCD.  Measured on the K2 fp8 layer:
+  // down 1-2 % faster than slab-major (T = 512..8192); gate_up on the
+  // current kernel 1.2 % faster at T = 2048 and 4096 (FETCH_SIZE -16 % at
+  // T = 4096), unchanged at 512 and 1024.
+  const int tix = v / slabs;
+  const int slab = v - tix * slabs;
+  const Tile tl = a.tiles[tix];
+  if (tl.group == a.E)
+    tile_fp8_body<MODE, false>(a, slab, tl, ws0, ws1, ws2, ws3, ws4, ws5, xs0, xs1, xs2, wscale);
+  else
+    tile_fp8_body<MODE, WNT>(a, slab, tl, ws0, ws1, ws2, ws3, ws4, ws5, xs0, xs1, xs2, wscale);
 }
 
 // The row scales of the grouped rows of the tiled fp8 gate_up in
