@@ -66,26 +66,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // `ks` > 1 splits the K loop over ks blocks (few work items): each writes its
 // fp32 partial sums to a.part, and ffn_split_finish adds them up in part
 // order and applies the epilogue.
-// WNT: the weight DMA carries the nontemporal hint (each weight slab is
-// expected to be read by one tile only).
+// The body of one block's work item (K part kp of slab `slab` of tile tl).
+// WNT: the weight DMA carries the nontemporal hint.  The LDS stages are the
+// kernel's (one allocation for both copies of this body that it inlines).
 template <int MODE, bool WNT>
-__global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int ks) {
-  // two stages as separate objects: the compiler then knows that a DMA into
-  // one stage does not alias LDS reads of the other
-  // weights: [stage][m-tile][wave's 32 rows x 128 B]; tokens: [stage][128 rows x 128 B]
-  __shared__ __attribute__((aligned(16))) uint8_t wst[2][4][4 * 32 * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t tst[2][kBM * kRowB];
-  // ---- XCD-chunked mapping of this block to (K part, slab, tile) ----
-  const int ntile = *a.tile_count;
-  const int total = slabs * ntile * ks;
-  const int per = (total + kXcd - 1) / kXcd;
-  const int j = blockIdx.x / kXcd;
-  const int v0 = (blockIdx.x % kXcd) * per + j;
-  if (j >= per || v0 >= total) return;
-  const int kp = v0 / (slabs * ntile);
-  const int v = v0 - kp * (slabs * ntile);
-  const int slab = v / ntile;
-  const Tile tl = a.tiles[v - slab * ntile];
+__device__ __forceinline__ void tile_bf16_body(const FfnArgs& a, int ks, int kp, int slab, const Tile& tl,
+                                               uint8_t (&wst)[2][4][4 * 32 * kRowB],
+                                               uint8_t (&tst)[2][kBM * kRowB]) {
   const bool sh = tl.group == a.E;
   const int Fg = sh ? a.Fs : a.F;
   const int64_t TK = static_cast<int64_t>(a.T) * a.k;
@@ -359,6 +346,35 @@ __global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int k
   else if (nn == 3) run(std::integral_constant<int, 3>{});
   else if (nn == 2) run(std::integral_constant<int, 2>{});
   else run(std::integral_constant<int, 1>{});
+}
+
+// WNT: the weight DMA of routed tiles carries the nontemporal hint (each
+// routed weight slab is expected to be read by one tile only); never that
+// of the shared expert, whose slabs every token tile reads.  The block
+// branches once, on its tile, between two inlined copies of the body.
+template <int MODE, bool WNT>
+__global__ __launch_bounds__(256) void ffn_tile_bf16(FfnArgs a, int slabs, int ks) {
+  // two stages as separate objects: the compiler then knows that a DMA into
+  // one stage does not alias LDS reads of the other
+  // weights: [stage][m-tile][wave's 32 rows x 128 B]; tokens: [stage][128 rows x 128 B]
+  __shared__ __attribute__((aligned(16))) uint8_t wst[2][4][4 * 32 * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t tst[2][kBM * kRowB];
+  // ---- XCD-chunked mapping of this block to (K part, slab, tile) ----
+  const int ntile = *a.tile_count;
+  const int total = slabs * ntile * ks;
+  const int per = (total + kXcd - 1) / kXcd;
+  const int j = blockIdx.x / kXcd;
+  const int v0 = (blockIdx.x % kXcd) * per + j;
+  if (j >= per || v0 >= total) return;
+  const int kp = v0 / (slabs * ntile);
+  const int v = v0 - kp * (slabs * ntile);
+  const int slab = v / ntile;
+  const Tile tl = a.tiles[v - slab * ntile];
+  // (without the hint one copy serves every tile)
+  if (WNT && tl.group != a.E)
+    tile_bf16_body<MODE, WNT>(a, ks, kp, slab, tl, wst, tst);
+  else
+    tile_bf16_body<MODE, false>(a, ks, kp, slab, tl, wst, tst);
 }
 
 // Sum of the K-part partials of each grouped row in part order, then the

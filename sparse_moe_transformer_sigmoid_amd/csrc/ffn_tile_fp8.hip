@@ -443,10 +443,11 @@ __global__ __launch_bounds__(512) void ffn_tile_fp8(FfnArgs a, int slabs) {
   const int tix = v / slabs;
   const int slab = v - tix * slabs;
   const Tile tl = a.tiles[tix];
-  if (tl.group == a.E)
-    tile_fp8_body<MODE, false>(a, slab, tl, ws0, ws1, ws2, ws3, ws4, ws5, xs0, xs1, xs2, wscale);
-  else
+  // (without the hint one copy serves every tile)
+  if (WNT && tl.group != a.E)
     tile_fp8_body<MODE, WNT>(a, slab, tl, ws0, ws1, ws2, ws3, ws4, ws5, xs0, xs1, xs2, wscale);
+  else
+    tile_fp8_body<MODE, false>(a, slab, tl, ws0, ws1, ws2, ws3, ws4, ws5, xs0, xs1, xs2, wscale);
 }
 
 // The row scales of the grouped rows of the tiled fp8 gate_up in
