@@ -57,7 +57,9 @@ struct Frag8 {
   float bs[NT];
 };
 
-template <int NA, int NT>
+// NTW: the weight loads carry the nontemporal hint (a routed tile's; not
+// the shared expert's, whose slabs every token tile reads)
+template <int NA, int NT, bool NTW>
 __device__ __forceinline__ void load_frag8(Frag8<NA, NT>& f, const uint8_t* const (&pa)[NA],
                                            const float* const (&wsc)[NA],
                                            const uint8_t* const (&pb)[NT],
@@ -65,8 +67,10 @@ __device__ __forceinline__ void load_frag8(Frag8<NA, NT>& f, const uint8_t* cons
   const int koff = s * 128;
 #pragma unroll
   for (int m = 0; m < NA; ++m) {
-    f.a[m][0] = load_nt(reinterpret_cast<const uint4*>(pa[m] + koff));
-    f.a[m][1] = load_nt(reinterpret_cast<const uint4*>(pa[m] + ld8 + koff));
+    const uint4* w0 = reinterpret_cast<const uint4*>(pa[m] + koff);
+    const uint4* w1 = reinterpret_cast<const uint4*>(pa[m] + ld8 + koff);
+    f.a[m][0] = NTW ? load_nt(w0) : *w0;
+    f.a[m][1] = NTW ? load_nt(w1) : *w1;
     f.ws[m] = wsc[m][s];
   }
 #pragma unroll
@@ -122,14 +126,27 @@ __device__ __forceinline__ void mma_frag8(const Frag8<NA, NT>& f, uint4 (*scr)[1
 // LDS in wave order (wave 0 keeps them).  pa[m]: this lane's load position
 // in tile m (row L / 8, byte 16 (L % 8)); ld8: 8 rows in bytes; pb[n]: token
 // row r + 16 q.
+// The K loop's LDS (per-wave layout scratch, partial-sum exchange): one
+// allocation per shape, shared by both copies of the loop a kernel inlines.
 template <int NA, int NT>
+struct StreamLds8 {
+  uint4 scr[kWK][NA][16][8];
+  f32x4 red[kWK - 1][NA][NT][64];
+};
+template <int NA, int NT>
+__device__ __forceinline__ StreamLds8<NA, NT>& stream_lds8() {
+  __shared__ StreamLds8<NA, NT> l;
+  return l;
+}
+
+template <int NA, int NT, bool NTW>
 __device__ __forceinline__ void stream_k_fp8(const uint8_t* const (&pa)[NA],
                                              const float* const (&wsc)[NA],
                                              const uint8_t* const (&pb)[NT],
                                              const float* const (&bsc)[NT], int64_t ld8, int steps,
                                              f32x4 (&acc)[NA][NT]) {
-  __shared__ uint4 scr[kWK][NA][16][8];
-  __shared__ f32x4 red[kWK - 1][NA][NT][64];
+  auto& scr = stream_lds8<NA, NT>().scr;
+  auto& red = stream_lds8<NA, NT>().red;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int m = 0; m < NA; ++m)
@@ -137,11 +154,11 @@ __device__ __forceinline__ void stream_k_fp8(const uint8_t* const (&pa)[NA],
     for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   int s = wave;
   Frag8<NA, NT> cur, nxt;
-  if (s < steps) load_frag8(cur, pa, wsc, pb, bsc, ld8, s);
+  if (s < steps) load_frag8<NA, NT, NTW>(cur, pa, wsc, pb, bsc, ld8, s);
 #pragma unroll 1
   while (s < steps) {
     const int sn = s + kWK;
-    if (sn < steps) load_frag8(nxt, pa, wsc, pb, bsc, ld8, sn);
+    if (sn < steps) load_frag8<NA, NT, NTW>(nxt, pa, wsc, pb, bsc, ld8, sn);
     mma_frag8(cur, scr[wave], acc);
     cur = nxt;
     s = sn;
@@ -214,7 +231,11 @@ __global__ __launch_bounds__(256) void gate_up_stream_fp8(FfnArgs a) {
     bsc[n] = sbase + row * KB;
   }
   f32x4 acc[2 * NF][NT];
-  stream_k_fp8<2 * NF>(pa, wsc, pb, bsc, 8 * H, static_cast<int>(KB), acc);
+  // (one branch per block between two copies of the K loop)
+  if (sh)
+    stream_k_fp8<2 * NF, NT, false>(pa, wsc, pb, bsc, 8 * H, static_cast<int>(KB), acc);
+  else
+    stream_k_fp8<2 * NF, NT, true>(pa, wsc, pb, bsc, 8 * H, static_cast<int>(KB), acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -266,7 +287,10 @@ __global__ __launch_bounds__(256) void down_stream_fp8(FfnArgs a) {
     }
   }
   f32x4 acc[2][NT];
-  stream_k_fp8<2>(pa, wsc, pb, bsc, 8 * static_cast<int64_t>(Fg), static_cast<int>(KB), acc);
+  // (one copy of the K loop, every weight load with the hint: a second copy
+  // for the shared tiles cost this kernel registers and occupancy, K2 fp8
+  // T=128 down 0.687 -> 0.702 ms)
+  stream_k_fp8<2, NT, true>(pa, wsc, pb, bsc, 8 * static_cast<int64_t>(Fg), static_cast<int>(KB), acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {

@@ -46,14 +46,18 @@ struct Frag {
   uint4 b[NT][KS / 32];
 };
 
-template <int NA, int NT, int KS>
+// NTW: the weight loads carry the nontemporal hint (weights read once: a
+// routed tile's; not the shared expert's, whose slabs every token tile reads)
+template <int NA, int NT, int KS, bool NTW>
 __device__ __forceinline__ void load_frag(Frag<NA, NT, KS>& f, const uint16_t* const (&pa)[NA],
                                           const uint16_t* const (&pb)[NT], int64_t ld8, int koff) {
 #pragma unroll
   for (int m = 0; m < NA; ++m)
 #pragma unroll
-    for (int j = 0; j < KS / 32; ++j)
-      f.a[m][j] = load_nt(reinterpret_cast<const uint4*>(pa[m] + (j & 1) * ld8 + koff + (j >> 1) * 64));
+    for (int j = 0; j < KS / 32; ++j) {
+      const uint4* w = reinterpret_cast<const uint4*>(pa[m] + (j & 1) * ld8 + koff + (j >> 1) * 64);
+      f.a[m][j] = NTW ? load_nt(w) : *w;
+    }
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const uint4* s = reinterpret_cast<const uint4*>(pb[n] + koff);
@@ -112,13 +116,26 @@ __device__ __forceinline__ void mma_frag(const Frag<NA, NT, KS>& f, uint4 (*scr)
 // the total.  pa[m]: this lane's load position in weight tile m (row L / 8,
 // byte 16 (L % 8)); ld8: 8 rows, in elements; pb[n]: token row r + 8 q.
 // Both operands use the same K order, so the MFMA sums run over the full step.
+// The K loop's LDS (per-wave layout scratch, partial-sum exchange): one
+// allocation per shape, shared by both copies of the loop a kernel inlines.
 template <int NA, int NT, int KS>
+struct StreamLds {
+  uint4 scr[kWK][NA][16][KS / 8];
+  f32x4 red[kWK - 1][NA][NT][64];
+};
+template <int NA, int NT, int KS>
+__device__ __forceinline__ StreamLds<NA, NT, KS>& stream_lds() {
+  __shared__ StreamLds<NA, NT, KS> l;
+  return l;
+}
+
+template <int NA, int NT, int KS, bool NTW>
 __device__ __forceinline__ void stream_k(const uint16_t* const (&pa)[NA],
                                          const uint16_t* const (&pb)[NT], int64_t ld8, int steps,
                                          f32x4 (&acc)[NA][NT]) {
   static_assert(KS == 128 || KS == 64, "K step of one or two 128-byte lines per row");
-  __shared__ uint4 scr[kWK][NA][16][KS / 8];
-  __shared__ f32x4 red[kWK - 1][NA][NT][64];
+  auto& scr = stream_lds<NA, NT, KS>().scr;
+  auto& red = stream_lds<NA, NT, KS>().red;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int m = 0; m < NA; ++m)
@@ -126,11 +143,11 @@ __device__ __forceinline__ void stream_k(const uint16_t* const (&pa)[NA],
     for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   int s = wave;
   Frag<NA, NT, KS> cur, nxt;
-  if (s < steps) load_frag(cur, pa, pb, ld8, s * KS);
+  if (s < steps) load_frag<NA, NT, KS, NTW>(cur, pa, pb, ld8, s * KS);
 #pragma unroll 1
   while (s < steps) {
     const int sn = s + kWK;
-    if (sn < steps) load_frag(nxt, pa, pb, ld8, sn * KS);
+    if (sn < steps) load_frag<NA, NT, KS, NTW>(nxt, pa, pb, ld8, sn * KS);
     mma_frag(cur, scr[wave], acc);
     cur = nxt;
     s = sn;
@@ -194,7 +211,11 @@ __global__ __launch_bounds__(256) void gate_up_stream_bf16(FfnArgs a) {
     pb[n] = b + q * 8;
   }
   f32x4 acc[2 * NF][NT];
-  stream_k<2 * NF, NT, KS>(pa, pb, 8 * H, a.H / KS, acc);
+  // (one branch per block between two copies of the K loop)
+  if (sh)
+    stream_k<2 * NF, NT, KS, false>(pa, pb, 8 * H, a.H / KS, acc);
+  else
+    stream_k<2 * NF, NT, KS, true>(pa, pb, 8 * H, a.H / KS, acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -236,7 +257,10 @@ __global__ __launch_bounds__(256) void down_stream_bf16(FfnArgs a) {
                 : static_cast<const uint16_t*>(a.h) + p * a.F) + q * 8;
   }
   f32x4 acc[NA][NT];
-  stream_k<NA, NT, KS>(pa, pb, 8 * static_cast<int64_t>(Fg), Fg / KS, acc);
+  if (sh)
+    stream_k<NA, NT, KS, false>(pa, pb, 8 * static_cast<int64_t>(Fg), Fg / KS, acc);
+  else
+    stream_k<NA, NT, KS, true>(pa, pb, 8 * static_cast<int64_t>(Fg), Fg / KS, acc);
   if ((threadIdx.x >> 6) != 0) return;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
