@@ -17,8 +17,9 @@
 // Each wave's loads for its next K step (operands and scales) are issued
 // before the current step's MFMAs, so a load's latency overlaps a step of
 // compute instead of stalling every step.  As in the bf16 stream, weights
-// are loaded in whole 128-byte lines with the nontemporal hint and pass
-// through a per-wave LDS scratch into the MFMA layout.
+// are loaded in whole 128-byte lines with the nontemporal hint (gate_up: not
+// the shared expert's) and pass through a per-wave LDS scratch into the
+// MFMA layout.
 // The SwiGLU output is written in fp32; one activation-quant launch turns the
 // routed and shared rows into e4m3 codes + per-128 scales for the down
 // projection.

@@ -11,7 +11,8 @@
 // 16 gate + 16 up rows) or 64-row (down; 32-row for 64-row work items)
 // weight slab, K steps of 128 (64 for 64-row items) dealt round-robin to
 // the waves.  The weights are loaded in whole 128-byte lines per instruction
-// with the nontemporal hint and pass through a per-wave LDS scratch into the
+// (with the nontemporal hint, except the shared expert's, whose slabs every
+// token tile reads) and pass through a per-wave LDS scratch into the
 // MFMA layout (16x16x32 bf16; the K order inside a step permuted the same way
 // for both operands); each weight byte is read exactly once per tile of 16
 // rows.  The four partial sums
